@@ -1,0 +1,151 @@
+"""Throughput of the RoPE-aware rotated INT4 attention path on one MI355X.
+
+One step = the whole hot path on one batch already resident in HBM:
+rotattn_quantize_qk (3D RoPE + Walsh-Hadamard + per-block INT4 Q/K) ->
+rotattn_quantize_v (per-channel INT4 V + column sums) -> rotattn_attention
+(fused INT4 flash loop, FP16 fallback tiles and merge when routing is on).
+
+Metric: attention TOPS = 4 B H L^2 D / step time (D the nominal head dim),
+on the 720p-style workload (B=1, H=40, L=75600, D=128). The roofline entry
+reports the INT4 attention kernel alone against the INT8 matrix-core peak
+(5.0 POP/s dense). The CPU baseline is the oracle (numpy) on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention TOPS (4·B·H·L²·D/s) and % of INT8 MFMA peak, 75600-token 40-head"
+INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 matrix-core peak, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0
+
+
+def cpu_baseline(w: W.Workload, x, rows_sample: int = 1024):
+    """Oracle (numpy, 1 BLAS thread) on head 0: its prologue plus the flash loop for `rows_sample` query rows."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import core as O
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        q, k, v = x["q"][0, 0], x["k"][0, 0], x["v"][0, 0]
+        qp = O.qk_prologue(q, w.prefix, w.grid, w.split, w.base, w.rotation)
+        kp = O.qk_prologue(k, w.prefix, w.grid, w.split, w.base, w.rotation)
+        vc, sv, cs = O.quantize_v(v)
+        rows = np.arange(min(rows_sample, w.L))
+        O.int4_flash_rows(qp["codes"], qp["scale"], kp["codes"], kp["scale"], vc, sv, cs, w.L, w.D, rows)
+        dt = time.perf_counter() - t0
+    ops = 4.0 * rows.size * w.L * w.D
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"head 0 of {w.name}: Q/K/V prologue of all {w.L} tokens + INT4 flash loop for "
+                      f"{rows.size} query rows over all keys ({dt:.1f} s; ops credited for the rows only)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p", choices=list(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is design only "
+                                   "(per-head split, see DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import int4_quantized_flashattention_amd as R
+
+    w = W.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    x = W.full_inputs(w, threads=16)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(x["q"]).to(dev)
+    k = torch.from_numpy(x["k"]).to(dev)
+    v = torch.from_numpy(x["v"]).to(dev)
+    mask_np = W.head_fallback_mask(w)
+    mask = torch.from_numpy(mask_np).to(dev) if mask_np is not None else None
+    p = R.problem_from_workload(w)
+    need_rope = mask is not None or np.isfinite(w.tau)
+    qk = R.binding.alloc_qk(p, dev, need_rope)
+    vq = R.binding.alloc_v(p, dev)
+    out = torch.empty((w.B, w.H, w.L, w.D), dtype=torch.float16, device=dev)
+    ws = {c: (torch.empty(max(1, R.workspace_bytes(p, c)), dtype=torch.uint8, device=dev))
+          for c in (R.binding.CALL_QUANTIZE_QK, R.binding.CALL_QUANTIZE_V, R.binding.CALL_ATTENTION)}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        R.rotattn_quantize_qk(p, q, k, out=qk, ws=ws[0], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        R.rotattn_quantize_v(p, v, out=vq, ws=ws[1], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        R.rotattn_attention(p, qk, vq, v=v if need_rope else None, head_fallback=mask, out=out, ws=ws[2],
+                            stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_qk = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_v = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    t_att = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    ms_per_step = float(t_step.mean())
+    ops = w.credited_ops()
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    att_ms = float(t_att.mean())
+    achieved = ops / (att_ms * 1e-3) / 1e12
+    s = R.get_sizes(p)
+    # compulsory HBM bytes of the prologue: fp16 Q and K in, codes + scales + flags out
+    qk_bytes = 2 * w.B * w.H * w.L * w.D * 2 + 2 * s.qk_codes_bytes + 2 * s.qk_scale_bytes + 2 * s.qk_flag_bytes
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} L={w.L} D={w.D} grid={'x'.join(map(str, w.grid))} "
+                               f"prefix={w.prefix} rotation={'group64' if w.rotation else 'full'}",
+                   "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.D, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "int4_attn_kernel (rotattn_attention)", "avg_ms": round(att_ms, 4)},
+        "breakdown_ms": {"quantize_qk": round(float(t_qk.mean()), 4), "quantize_v": round(float(t_v.mean()), 4),
+                         "attention": round(att_ms, 4),
+                         "prologue_qk_GBps": round(qk_bytes / (t_qk.mean() * 1e-3) / 1e9, 1)},
+        "wall_s_timed": round(wall, 3), "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_rows)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

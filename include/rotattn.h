@@ -1,0 +1,212 @@
+/*
+ * rotattn: RoPE-aware-rotated mixed-precision INT4 FlashAttention for
+ * video-DiT self-attention with 3D RoPE, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one the RotateAttention abstract (arXiv 2607.02584)
+ * describes: 3D RoPE on Q and K, an orthonormal Walsh-Hadamard rotation
+ * applied after RoPE (the "negligible-overhead" variant of its RoPE-aware
+ * rotation), symmetric INT4 Q/K/V, a fused flash loop with integer Q.K^T,
+ * float32 online softmax and the range-optimized P quantization (fixed scale
+ * 1/15, zero-point -8), and selective FP16 fallback for accuracy-sensitive
+ * blocks, heads and denoising steps. The flash loop follows the online-softmax
+ * recurrences and the block mask of RainFusion2.0, section 3.1 "Blockwise
+ * Sparse".
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are device (HBM) addresses that the caller
+ *    allocates and owns. The library never allocates or frees memory and
+ *    keeps no mutable global state; all scratch lives in the caller's
+ *    workspace (size from rotattn_workspace_bytes).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream). No call synchronizes with the host.
+ *  - Return ROTATTN_OK (0) on success or a negative ROTATTN_E* code.
+ *    Argument errors are detected on the host before anything is enqueued
+ *    and leave every output untouched. ROTATTN_ELAUNCH reports a failed
+ *    kernel launch (from hipGetLastError); outputs are then undefined.
+ *  - Inputs are not checked for NaN or Inf.
+ *  - Attention is non-causal (video-DiT self-attention).
+ *
+ * Shapes: B batch, H heads, L tokens, D head dim (64 or 128). Tokens are the
+ * text prefix (no RoPE) followed by the video latent grid grid_t x grid_h x
+ * grid_w flattened frame-major, the default [F, H, W] order of RainFusion2.0
+ * ("3D Window Permutation"). Lp = L rounded up to a multiple of 64,
+ * NB = Lp / 64, D' = D for ROTATTN_ROT_FULL and 192 for ROTATTN_ROT_GROUP64.
+ */
+#ifndef ROTATTN_H
+#define ROTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROTATTN_VERSION 1
+
+/* error codes */
+#define ROTATTN_OK            0
+#define ROTATTN_EINVAL       -1  /* null pointer, bad size, split or stride */
+#define ROTATTN_EUNSUPPORTED -2  /* head dim other than 64 or 128; a RoPE group wider than 64 with ROT_GROUP64 */
+#define ROTATTN_EALIGN       -3  /* a pointer or row stride not 16-byte aligned */
+#define ROTATTN_EWORKSPACE   -4  /* workspace missing or smaller than rotattn_workspace_bytes */
+#define ROTATTN_ELAUNCH      -5  /* a kernel launch failed */
+
+/* rotation applied after RoPE (RotateAttention abstract, "RoPE-aware Rotation") */
+#define ROTATTN_ROT_FULL    0  /* x' = x H_D / sqrt(D) over the whole head dim; D' = D */
+#define ROTATTN_ROT_GROUP64 1  /* each RoPE group zero padded to 64 and turned by H_64 / 8; D' = 192 */
+
+/* calls, for rotattn_workspace_bytes */
+#define ROTATTN_CALL_QUANTIZE_QK 0
+#define ROTATTN_CALL_QUANTIZE_V  1
+#define ROTATTN_CALL_ATTENTION   2
+#define ROTATTN_CALL_FORWARD     3
+#define ROTATTN_CALL_FP16_FORWARD 4
+#define ROTATTN_CALL_DEBUG_DUMP  5
+
+typedef void* rotattn_stream_t; /* hipStream_t */
+
+/* Problem description, passed by pointer to every call (host memory, read only). */
+typedef struct rotattn_problem {
+  int32_t B, H, L, D;
+  int32_t grid_t, grid_h, grid_w;  /* video latent grid; L = text_prefix + grid_t*grid_h*grid_w */
+  int32_t text_prefix;             /* leading text tokens that take no RoPE */
+  int32_t rope_split[3];           /* head dims of the t, h, w RoPE groups, contiguous, sum = D */
+  int32_t rotation;                /* ROTATTN_ROT_FULL or ROTATTN_ROT_GROUP64 */
+  double rope_base;                /* RoPE frequency base (10000) */
+  int64_t stride_b, stride_h, stride_l; /* element strides of q, k, v and out; the D axis is contiguous */
+  float block_err_tau;             /* a Q/K block whose quantization NSR exceeds this runs on FP16; +inf: never */
+  int32_t reserved;
+} rotattn_problem;
+
+/* Outputs of rotattn_quantize_qk, inputs of rotattn_attention / rotattn_forward. All device. */
+typedef struct rotattn_qk_buffers {
+  uint8_t* q_codes;     /* [B][H][Lp][D'/2]: byte k = dim 2k (low nibble) | dim 2k+1 (high nibble), two's complement INT4 */
+  uint8_t* k_codes;     /* same layout */
+  float* q_scale;       /* [B][H][NB] per-64-token-block scale s = absmax/7 */
+  float* k_scale;
+  uint8_t* q_flag;      /* [B][H][NB] 1 if the block's quantization NSR > block_err_tau */
+  uint8_t* k_flag;
+  uint32_t* head_kflag; /* [B*H] nonzero if any K block of the head is flagged */
+  void* q_rope;         /* optional fp16 [B][H][L][D] (dense): RoPE'd, unrotated Q for the FP16 path; NULL = not written */
+  void* k_rope;         /* optional, as q_rope */
+} rotattn_qk_buffers;
+
+/* Quantized V. All device. */
+typedef struct rotattn_v_buffers {
+  uint8_t* v_codes;  /* [B][H][NB][D][32]: the 64 keys of one block and channel, nibble packed in the order the
+                        INT4 kernel's matrix-core operands use: byte 16*hh + 8*s + 4*w + b holds, in its low
+                        nibble, the code of key 32*s + 16*w + 4*hh + b and, in its high nibble, the code of key
+                        32*s + 16*w + 8 + 4*hh + b (hh, s, w in {0,1}, b in 0..3) */
+  float* v_scale;    /* [B][H][D] per-channel scale s_v = absmax over the L tokens / 7 */
+  int32_t* v_colsum; /* [B][H][NB][D] integer sum of the 64 codes of each key block and channel */
+} rotattn_v_buffers;
+
+/* Buffer sizes in bytes for a problem (host only, no device work). */
+typedef struct rotattn_sizes {
+  int64_t Lp, NB, Dp;
+  int64_t qk_codes_bytes;  /* each of q_codes, k_codes */
+  int64_t qk_scale_bytes;  /* each of q_scale, k_scale */
+  int64_t qk_flag_bytes;   /* each of q_flag, k_flag */
+  int64_t head_flag_bytes; /* head_kflag */
+  int64_t rope_bytes;      /* each of q_rope, k_rope */
+  int64_t v_codes_bytes, v_scale_bytes, v_colsum_bytes;
+  int64_t out_min_elems;   /* smallest element count an output buffer with the problem's strides spans */
+} rotattn_sizes;
+
+/* Library version (ROTATTN_VERSION). */
+int rotattn_version(void);
+
+/* Static message for an error code; never NULL. */
+const char* rotattn_strerror(int code);
+
+/* Validate `p` and fill `out` with the buffer sizes. Errors: EINVAL, EUNSUPPORTED. */
+int rotattn_get_sizes(const rotattn_problem* p, rotattn_sizes* out);
+
+/* Workspace bytes that call `call` (ROTATTN_CALL_*) needs for `p`. Errors: EINVAL, EUNSUPPORTED. */
+int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes);
+
+/*
+ * Steps 1-3 for Q and K (RotateAttention abstract): 3D RoPE (float32, each
+ * pair turned by pos * base^(-2i/g_rot) of its axis group), the
+ * Walsh-Hadamard rotation, symmetric INT4 quantization per 64-token block
+ * (s = absmax/7, codes clamp(rne(x/s), -7, 7)) and the block error flags
+ * (NSR = |x - s c|^2 / |x|^2 > block_err_tau).
+ * q, k: device fp16 with the problem's strides, 16-byte aligned rows.
+ * out: codes, scales, flags, head_kflag (all required); q_rope/k_rope
+ * optional (required later by rotattn_attention when FP16 fallback can occur).
+ * Workspace: ROTATTN_CALL_QUANTIZE_QK bytes (RoPE tables).
+ */
+int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k,
+                        const rotattn_qk_buffers* out, void* workspace, size_t workspace_bytes,
+                        rotattn_stream_t stream);
+
+/*
+ * Per-channel symmetric INT4 quantization of V over all L tokens of a head,
+ * with per-64-key-block column sums (the zero-point correction term of the
+ * P.V product). v: device fp16 with the problem's strides.
+ * Workspace: ROTATTN_CALL_QUANTIZE_V bytes.
+ */
+int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_buffers* out,
+                       void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
+
+/*
+ * Step 4 and the FP16 fallback, from quantized inputs: the fused INT4 flash
+ * loop (RainFusion2.0 sec. 3.1 recurrences in the log2 domain) with integer
+ * Q.K^T on the matrix cores, float32 online softmax, P codes
+ * pq = rne(15 P) - 8, and integer P.V against the per-channel V codes with
+ * the 8 * column-sum zero-point correction; output
+ * out = O * (s_v / 15) / l in fp16.
+ * Routing (selective FP16 fallback): tile (query block i, key block j) runs
+ * on the FP16 path when head_fallback[b*H+h] != 0, or q_flag[i], or
+ * k_flag[j]; query blocks that mix both paths merge the two partial results
+ * by log-sum-exp.
+ * head_fallback: device uint8 [B*H] or NULL (no head is masked). When it is
+ * non-NULL or block_err_tau is finite, qk->q_rope and qk->k_rope and v are
+ * required (the FP16 path reads them); otherwise they may be NULL.
+ * out: device fp16 with the problem's strides (may not alias inputs).
+ * Workspace: ROTATTN_CALL_ATTENTION bytes.
+ */
+int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
+                      const void* v, const uint8_t* head_fallback, void* out,
+                      void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
+
+/*
+ * rotattn_quantize_v into the workspace followed by rotattn_attention: the
+ * whole attention call after rotattn_quantize_qk.
+ * Workspace: ROTATTN_CALL_FORWARD bytes.
+ */
+int rotattn_forward(const rotattn_problem* p, const rotattn_qk_buffers* qk, const void* v,
+                    const uint8_t* head_fallback, void* out,
+                    void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
+
+/*
+ * Whole-call FP16 flash attention with 3D RoPE, no rotation or quantization:
+ * the fallback for a whole denoising step (RotateAttention abstract).
+ * Workspace: ROTATTN_CALL_FP16_FORWARD bytes (RoPE tables and RoPE'd copies).
+ */
+int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k, const void* v, void* out,
+                         void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
+
+/*
+ * Test hook: runs the INT4 flash kernel, instantiated with its dump switch,
+ * on selected 64-row query blocks and writes its intermediate integers.
+ * units: device int32 [n_units], unit = (b*H + h)*NB + query_block.
+ * Outputs (device, caller zero-fills; blocks skipped by routing stay untouched):
+ *   acc_qk  int32 [n_units][64][Lp]   integer q.k over the rotated dims
+ *   p_codes int8  [n_units][64][Lp]   pq in [-8, 7]
+ *   acc_pv  int32 [n_units][64][NB][D] sum over the block of (pq + 8) * v_code
+ *                                      (= pq . v + 8 * colsum)
+ *   m_hist  float [n_units][64][NB]   running max (log2 domain) after each block
+ * Rows at or beyond L are not written. head_fallback as in rotattn_attention.
+ */
+int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
+                       const uint8_t* head_fallback, const int32_t* units, int32_t n_units,
+                       int32_t* acc_qk, int8_t* p_codes, int32_t* acc_pv, float* m_hist,
+                       rotattn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROTATTN_H */

@@ -1,0 +1,294 @@
+// Q/K prologue: 3D RoPE -> Walsh-Hadamard rotation -> per-64-token INT4
+// quantization with nibble-packed stores and the block error flag.
+//
+// Method: RotateAttention abstract (arXiv 2607.02584) -- 3D RoPE on Q and K,
+// a RoPE-aware orthonormal rotation applied after RoPE (here the online
+// Walsh-Hadamard variant), symmetric INT4 quantization, and selective FP16
+// fallback for blocks whose quantization error is too large.
+//
+// One workgroup of 256 threads handles one 64-token block of one (b, h,
+// tensor). The block is read once with 16-byte loads, rotated in registers
+// and LDS, and written once as nibble-packed codes: HBM traffic is the
+// compulsory 2 bytes in / D'/2 bytes out per token and head dim.
+//
+// Floating-point contract (both sides of the parity tests follow it): each
+// RoPE product and sum is rounded separately (no FMA; the library is built
+// with -ffp-contract=off and uses __fmul_rn and friends), the Hadamard
+// butterflies run in stage order h = 1, 2, 4, ..., then one multiply by
+// float(1/sqrt(n)); scale = absmax / 7 and code = rne(x / scale) with IEEE
+// division.
+#include "common.h"
+
+namespace rotattn {
+
+// cos/sin of every (axis, position, pair): angle = pos * base^(-2i / g_rot),
+// evaluated in double and rounded once to float. Also zeroes a small u32
+// array (the per-head flag summary) so that one launch prepares both.
+__global__ void rope_table_kernel(KProblem kp, float* tab, uint32_t* zero_u32, int n_zero) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (zero_u32 != nullptr && i < n_zero) zero_u32[i] = 0u;
+  int rem = i;
+  for (int a = 0; a < 3; ++a) {
+    const int npos = (a == 0) ? kp.T : (a == 1) ? kp.Hh : kp.W;
+    const int np = kp.npair[a];
+    const int n = npos * np;
+    if (rem < n) {
+      const int p = rem / np, pi = rem - (rem / np) * np;
+      const double th = pow(kp.base, -(2.0 * pi) / (double)(2 * np));
+      const double ang = (double)p * th;
+      tab[kp.tab_off[a] + rem] = (float)cos(ang);
+      tab[kp.tab_off[a] + n + rem] = (float)sin(ang);
+      return;
+    }
+    rem -= n;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_block_to_lds(const KProblem& kp, const __half* x, int b, int h, int blk,
+                                                  float (*Y)[D + 4]) {
+  constexpr int PER = D / 4;  // halves per thread (4 threads per token)
+  const int t = threadIdx.x;
+  const int tok = t >> 2, part = t & 3;
+  const int tg = blk * kBlock + tok;
+  float vals[PER];
+  if (tg < kp.L) {
+    const __half* src = x + (long long)b * kp.sb + (long long)h * kp.sh + (long long)tg * kp.sl + part * PER;
+#pragma unroll
+    for (int c = 0; c < PER / 8; ++c) {
+      uint4 u = reinterpret_cast<const uint4*>(src)[c];
+      const __half* hv = reinterpret_cast<const __half*>(&u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vals[c * 8 + e] = __half2float(hv[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) vals[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) Y[tok][part * PER + e] = vals[e];
+}
+
+// RoPE in place on the LDS tile: one task per (token, pair).
+template <int D>
+__device__ __forceinline__ void rope_lds(const KProblem& kp, const float* tab, int blk, float (*Y)[D + 4]) {
+  const int npt = kp.npair[0] + kp.npair[1] + kp.npair[2];
+  const int n0 = kp.T * kp.npair[0], n1 = kp.Hh * kp.npair[1], n2 = kp.W * kp.npair[2];
+  for (int task = threadIdx.x; task < kBlock * npt; task += blockDim.x) {
+    const int tok = task / npt;
+    int pr = task - tok * npt;
+    const int tg = blk * kBlock + tok;
+    if (tg >= kp.L || tg < kp.prefix) continue;
+    const int idx = tg - kp.prefix;
+    int a, pos, nA;
+    if (pr < kp.npair[0]) {
+      a = 0; pos = idx / (kp.Hh * kp.W); nA = n0;
+    } else if (pr < kp.npair[0] + kp.npair[1]) {
+      a = 1; pr -= kp.npair[0]; pos = (idx / kp.W) % kp.Hh; nA = n1;
+    } else {
+      a = 2; pr -= kp.npair[0] + kp.npair[1]; pos = idx % kp.W; nA = n2;
+    }
+    const float c = tab[kp.tab_off[a] + pos * kp.npair[a] + pr];
+    const float s = tab[kp.tab_off[a] + nA + pos * kp.npair[a] + pr];
+    const int d0 = kp.off[a] + 2 * pr;
+    const float x0 = Y[tok][d0], x1 = Y[tok][d0 + 1];
+    Y[tok][d0] = fsub_rn(fmul_rn(x0, c), fmul_rn(x1, s));
+    Y[tok][d0 + 1] = fadd_rn(fmul_rn(x0, s), fmul_rn(x1, c));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rope_copy(const KProblem& kp, int b, int h, int blk, float (*Y)[D + 4],
+                                                __half* dst) {
+  constexpr int PER = D / 4;
+  const int t = threadIdx.x;
+  const int tok = t >> 2, part = t & 3;
+  const int tg = blk * kBlock + tok;
+  if (tg >= kp.L) return;
+  __half* d = dst + ((long long)(b * kp.H + h) * kp.L + tg) * D + part * PER;
+#pragma unroll
+  for (int c = 0; c < PER / 8; ++c) {
+    uint4 u;
+    __half* hv = reinterpret_cast<__half*>(&u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = __float2half_rn(Y[tok][part * PER + c * 8 + e]);
+    reinterpret_cast<uint4*>(d)[c] = u;
+  }
+}
+
+__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Grid (NB, H, 2B): blockIdx.z = 2*b + tensor (0 = Q, 1 = K).
+template <int D, int ROT>
+__global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __half* q, const __half* k,
+                                                          const float* tab, QKOut o) {
+  constexpr int DP = (ROT == 1) ? 192 : D;
+  constexpr int N = (ROT == 1) ? 64 : D;       // Walsh-Hadamard size
+  constexpr int PARTS = DP / 32;               // 32-value chunks per token
+  constexpr int TASKS = kBlock * PARTS;        // multiple of 64
+  constexpr int ROUNDS = (TASKS + 255) / 256;
+  __shared__ float Y[kBlock][D + 4];
+  __shared__ float red[4];
+
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
+  const __half* x = tensor ? k : q;
+
+  load_block_to_lds<D>(kp, x, b, h, blk, Y);
+  __syncthreads();
+  rope_lds<D>(kp, tab, blk, Y);
+  __syncthreads();
+  __half* rcopy = tensor ? o.k_rope : o.q_rope;
+  if (rcopy != nullptr) store_rope_copy<D>(kp, b, h, blk, Y, rcopy);
+
+  // Walsh-Hadamard on 32-value chunks: stages 1..16 in registers, 32 and 64 across lanes.
+  float v[ROUNDS][32];
+  float amax = 0.f;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int task = threadIdx.x + 256 * r;
+    if (task < TASKS) {  // wave-uniform
+      const int tok = task / PARTS, part = task - (task / PARTS) * PARTS;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int p = 32 * part + e;
+        if (ROT == 1) {
+          const int g = p >> 6, oo = p & 63;
+          v[r][e] = (oo < kp.split[g]) ? Y[tok][kp.off[g] + oo] : 0.f;
+        } else {
+          v[r][e] = Y[tok][p];
+        }
+      }
+#pragma unroll
+      for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          if ((j & hs) == 0) {
+            const float a0 = v[r][j], b0 = v[r][j + hs];
+            v[r][j] = fadd_rn(a0, b0);
+            v[r][j + hs] = fsub_rn(a0, b0);
+          }
+        }
+      }
+#pragma unroll
+      for (int hs = 32; hs < N; hs <<= 1) {
+        const int mask = hs >> 5;
+        const bool upper = (part & mask) != 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float other = __shfl_xor(v[r][j], mask);
+          v[r][j] = upper ? fsub_rn(other, v[r][j]) : fadd_rn(v[r][j], other);
+        }
+      }
+      const float rn = (N == 128) ? 0.08838834764831845f : (N == 64) ? 0.125f : 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        v[r][j] = fmul_rn(v[r][j], rn);
+        amax = fmaxf(amax, fabsf(v[r][j]));
+      }
+    }
+  }
+  amax = block_reduce_max(amax, red);
+  const float s = fdiv_rn(amax, 7.0f);
+
+  float se = 0.f, sx = 0.f;
+  uint8_t* codes = tensor ? o.k_codes : o.q_codes;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int task = threadIdx.x + 256 * r;
+    if (task < TASKS) {
+      const int tok = task / PARTS, part = task - (task / PARTS) * PARTS;
+      uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        float c = 0.f;
+        if (s != 0.f) c = fminf(fmaxf(rintf(fdiv_rn(v[r][j], s)), -7.f), 7.f);
+        const float e = fsub_rn(v[r][j], fmul_rn(s, c));
+        se += e * e;
+        sx += v[r][j] * v[r][j];
+        const uint32_t nib = (uint32_t)((int)c) & 0xFu;
+        words[j >> 3] |= nib << (4 * (j & 7));
+      }
+      const int tg = blk * kBlock + tok;
+      uint8_t* dst = codes + ((long long)(b * kp.H + h) * kp.Lp + tg) * (DP / 2) + 16 * part;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+    }
+  }
+  se = block_reduce_sum(se, red);
+  sx = block_reduce_sum(sx, red);
+  if (threadIdx.x == 0) {
+    const long long bi = (long long)(b * kp.H + h) * kp.NB + blk;
+    (tensor ? o.k_scale : o.q_scale)[bi] = s;
+    const float nsr = (sx > 0.f) ? se / sx : 0.f;
+    const uint8_t flag = (nsr > kp.tau) ? 1 : 0;
+    (tensor ? o.k_flag : o.q_flag)[bi] = flag;
+    if (tensor == 1 && flag) atomicOr(&o.head_kflag[b * kp.H + h], 1u);
+  }
+}
+
+// RoPE only, into a dense fp16 copy (the input of the whole-call FP16 path).
+template <int D>
+__global__ __launch_bounds__(256) void rope_copy_kernel(KProblem kp, const __half* x, const float* tab,
+                                                        __half* dst) {
+  __shared__ float Y[kBlock][D + 4];
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  load_block_to_lds<D>(kp, x, b, h, blk, Y);
+  __syncthreads();
+  rope_lds<D>(kp, tab, blk, Y);
+  __syncthreads();
+  store_rope_copy<D>(kp, b, h, blk, Y, dst);
+}
+
+hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, hipStream_t s) {
+  int entries = 0;
+  entries += kp.T * kp.npair[0] + kp.Hh * kp.npair[1] + kp.W * kp.npair[2];
+  const int n = entries > n_zero ? entries : n_zero;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, kp, tab, zero_u32, n_zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half* k, const float* tab,
+                              const QKOut& o, hipStream_t s) {
+  dim3 grid(kp.NB, kp.H, 2 * kp.B);
+  if (kp.D == 128 && kp.rotation == 0)
+    hipLaunchKernelGGL((qk_prologue_kernel<128, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+  else if (kp.D == 128 && kp.rotation == 1)
+    hipLaunchKernelGGL((qk_prologue_kernel<128, 1>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+  else if (kp.D == 64 && kp.rotation == 0)
+    hipLaunchKernelGGL((qk_prologue_kernel<64, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+  else if (kp.D == 64 && kp.rotation == 1)
+    hipLaunchKernelGGL((qk_prologue_kernel<64, 1>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_copy(const KProblem& kp, const __half* x, const float* tab, __half* dst, hipStream_t s) {
+  dim3 grid(kp.NB, kp.H, kp.B);
+  if (kp.D == 128)
+    hipLaunchKernelGGL((rope_copy_kernel<128>), grid, dim3(256), 0, s, kp, x, tab, dst);
+  else if (kp.D == 64)
+    hipLaunchKernelGGL((rope_copy_kernel<64>), grid, dim3(256), 0, s, kp, x, tab, dst);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace rotattn

@@ -1,0 +1,362 @@
+// C ABI of the rotattn library: argument validation, buffer and workspace
+// sizing, and the launch sequence of each call. No device memory is
+// allocated here; every scratch buffer is carved out of the caller's
+// workspace.
+#include "../../include/rotattn.h"
+#include "common.h"
+
+#include <cmath>
+#include <cstring>
+
+using namespace rotattn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Derived {
+  KProblem kp;
+  int64_t Lp, NB, Dp;
+};
+
+int derive(const rotattn_problem* p, Derived* d) {
+  if (p == nullptr) return ROTATTN_EINVAL;
+  if (p->B < 1 || p->H < 1 || p->L < 0 || p->text_prefix < 0) return ROTATTN_EINVAL;
+  if (p->grid_t < 0 || p->grid_h < 0 || p->grid_w < 0) return ROTATTN_EINVAL;
+  if (p->D != 64 && p->D != 128) return ROTATTN_EUNSUPPORTED;
+  if (p->rotation != ROTATTN_ROT_FULL && p->rotation != ROTATTN_ROT_GROUP64) return ROTATTN_EINVAL;
+  const int64_t video = (int64_t)p->grid_t * p->grid_h * p->grid_w;
+  if ((int64_t)p->text_prefix + video != (int64_t)p->L) return ROTATTN_EINVAL;
+  if (p->L > (1 << 30)) return ROTATTN_EUNSUPPORTED;
+  int sum = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (p->rope_split[a] < 0) return ROTATTN_EINVAL;
+    sum += p->rope_split[a];
+  }
+  if (sum != p->D) return ROTATTN_EINVAL;
+  if (p->rotation == ROTATTN_ROT_GROUP64)
+    for (int a = 0; a < 3; ++a)
+      if (p->rope_split[a] > 64) return ROTATTN_EUNSUPPORTED;
+  if (!(p->rope_base > 0.0) || !std::isfinite(p->rope_base)) return ROTATTN_EINVAL;
+  if (std::isnan(p->block_err_tau)) return ROTATTN_EINVAL;
+  if (p->stride_l < p->D || p->stride_h < 0 || p->stride_b < 0) return ROTATTN_EINVAL;
+  if ((p->stride_l * 2) % 16 != 0 || (p->stride_h * 2) % 16 != 0 || (p->stride_b * 2) % 16 != 0)
+    return ROTATTN_EALIGN;
+
+  KProblem& k = d->kp;
+  std::memset(&k, 0, sizeof(k));
+  k.B = p->B; k.H = p->H; k.L = p->L; k.D = p->D;
+  k.Dp = (p->rotation == ROTATTN_ROT_GROUP64) ? 192 : p->D;
+  k.NB = (p->L + kBlock - 1) / kBlock;
+  k.Lp = k.NB * kBlock;
+  k.T = p->grid_t; k.Hh = p->grid_h; k.W = p->grid_w; k.prefix = p->text_prefix;
+  int off = 0, toff = 0;
+  const int npos[3] = {p->grid_t, p->grid_h, p->grid_w};
+  for (int a = 0; a < 3; ++a) {
+    k.split[a] = p->rope_split[a];
+    k.off[a] = off;
+    off += p->rope_split[a];
+    k.npair[a] = p->rope_split[a] / 2;
+    k.tab_off[a] = toff;
+    toff += 2 * npos[a] * k.npair[a];
+  }
+  k.tab_floats = toff;
+  k.rotation = p->rotation;
+  k.sb = p->stride_b; k.sh = p->stride_h; k.sl = p->stride_l;
+  k.tau = p->block_err_tau;
+  k.base = p->rope_base;
+  d->Lp = k.Lp; d->NB = k.NB; d->Dp = k.Dp;
+  return ROTATTN_OK;
+}
+
+// Workspace carve-up of every call. Offsets are 256-byte aligned.
+struct Layout {
+  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0;
+  size_t total = 0;
+};
+
+bool routes(const rotattn_problem* p) { return std::isfinite(p->block_err_tau); }
+
+Layout layout(const rotattn_problem* p, const Derived& d, int call) {
+  Layout L;
+  size_t o = 0;
+  const int64_t BH = (int64_t)p->B * p->H;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+  const size_t tab_bytes = (size_t)d.kp.tab_floats * sizeof(float) + 16;
+  const size_t vcodes_b = (size_t)BH * d.NB * p->D * 32;
+  const size_t vscale_b = (size_t)BH * p->D * sizeof(float);
+  const size_t vcolsum_b = (size_t)BH * d.NB * p->D * sizeof(int32_t);
+  const size_t absmax_b = (size_t)BH * p->D * sizeof(uint32_t);
+  const size_t po_b = (size_t)BH * d.Lp * p->D * sizeof(float);
+  const size_t pm_b = (size_t)BH * d.Lp * sizeof(float);
+  const size_t rope_b = (size_t)BH * p->L * p->D * 2;
+  switch (call) {
+    case ROTATTN_CALL_QUANTIZE_QK:
+      L.tab = take(tab_bytes);
+      break;
+    case ROTATTN_CALL_QUANTIZE_V:
+      L.absmax = take(absmax_b);
+      break;
+    case ROTATTN_CALL_ATTENTION:
+      if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
+      break;
+    case ROTATTN_CALL_FORWARD:
+      L.vcodes = take(vcodes_b); L.vscale = take(vscale_b); L.vcolsum = take(vcolsum_b);
+      L.absmax = take(absmax_b);
+      if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
+      break;
+    case ROTATTN_CALL_FP16_FORWARD:
+      L.tab = take(tab_bytes); L.qr = take(rope_b); L.kr = take(rope_b);
+      break;
+    case ROTATTN_CALL_DEBUG_DUMP:
+    default:
+      break;
+  }
+  L.total = o;
+  return L;
+}
+
+int check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (L.total == 0) return ROTATTN_OK;
+  if (ws == nullptr || ws_bytes < L.total) return ROTATTN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return ROTATTN_EALIGN;
+  return ROTATTN_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int launched(hipError_t e) { return e == hipSuccess ? ROTATTN_OK : ROTATTN_ELAUNCH; }
+
+int check_qk(const rotattn_qk_buffers* qk) {
+  if (qk == nullptr || !qk->q_codes || !qk->k_codes || !qk->q_scale || !qk->k_scale || !qk->q_flag ||
+      !qk->k_flag || !qk->head_kflag)
+    return ROTATTN_EINVAL;
+  if (!aligned16(qk->q_codes) || !aligned16(qk->k_codes)) return ROTATTN_EALIGN;
+  if ((qk->q_rope && !aligned16(qk->q_rope)) || (qk->k_rope && !aligned16(qk->k_rope))) return ROTATTN_EALIGN;
+  if (((uintptr_t)qk->q_scale & 3) || ((uintptr_t)qk->k_scale & 3) || ((uintptr_t)qk->head_kflag & 3))
+    return ROTATTN_EALIGN;
+  return ROTATTN_OK;
+}
+
+int check_v(const rotattn_v_buffers* vq) {
+  if (vq == nullptr || !vq->v_codes || !vq->v_scale || !vq->v_colsum) return ROTATTN_EINVAL;
+  if (!aligned16(vq->v_codes) || ((uintptr_t)vq->v_scale & 3) || ((uintptr_t)vq->v_colsum & 3))
+    return ROTATTN_EALIGN;
+  return ROTATTN_OK;
+}
+
+int attention_impl(const rotattn_problem* p, const Derived& d, const rotattn_qk_buffers* qk,
+                   const rotattn_v_buffers* vq, const void* v, const uint8_t* head_fallback, void* out,
+                   void* ws, const Layout& L, hipStream_t s) {
+  const bool route = routes(p);
+  const bool fp16_needed = route || head_fallback != nullptr;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_codes = qk->q_codes; a.k_codes = qk->k_codes;
+  a.q_scale = qk->q_scale; a.k_scale = qk->k_scale;
+  a.q_flag = qk->q_flag; a.k_flag = qk->k_flag; a.head_kflag = qk->head_kflag;
+  a.head_mask = head_fallback;
+  a.v_codes = vq->v_codes; a.v_scale = vq->v_scale;
+  a.q_rope = static_cast<const __half*>(qk->q_rope);
+  a.k_rope = static_cast<const __half*>(qk->k_rope);
+  a.v = static_cast<const __half*>(v);
+  a.out = static_cast<__half*>(out);
+  a.route = route;
+  if (route) { a.part_o = at<float>(ws, L.po); a.part_m = at<float>(ws, L.pm); a.part_l = at<float>(ws, L.pl); }
+  int rc = launched(launch_int4_attention(d.kp, a, false, s));
+  if (rc != ROTATTN_OK) return rc;
+  if (fp16_needed) rc = launched(launch_fp16_attention(d.kp, a, false, s));
+  return rc;
+}
+
+int check_attention_args(const rotattn_problem* p, const rotattn_qk_buffers* qk, const void* v,
+                         const uint8_t* head_fallback, const void* out) {
+  if (out == nullptr) return ROTATTN_EINVAL;
+  if (!aligned16(out)) return ROTATTN_EALIGN;
+  const bool fp16_needed = routes(p) || head_fallback != nullptr;
+  if (fp16_needed) {
+    if (v == nullptr || qk->q_rope == nullptr || qk->k_rope == nullptr) return ROTATTN_EINVAL;
+    if (!aligned16(v)) return ROTATTN_EALIGN;
+  }
+  return ROTATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rotattn_version(void) { return ROTATTN_VERSION; }
+
+const char* rotattn_strerror(int code) {
+  switch (code) {
+    case ROTATTN_OK: return "success";
+    case ROTATTN_EINVAL: return "invalid argument (null pointer, size, split, grid or stride)";
+    case ROTATTN_EUNSUPPORTED: return "unsupported problem (head dim must be 64 or 128; RoPE groups <= 64 for ROT_GROUP64)";
+    case ROTATTN_EALIGN: return "pointer or row stride not 16-byte aligned (workspace: 256-byte)";
+    case ROTATTN_EWORKSPACE: return "workspace missing or too small";
+    case ROTATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int rotattn_get_sizes(const rotattn_problem* p, rotattn_sizes* out) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (out == nullptr) return ROTATTN_EINVAL;
+  const int64_t BH = (int64_t)p->B * p->H;
+  out->Lp = d.Lp; out->NB = d.NB; out->Dp = d.Dp;
+  out->qk_codes_bytes = BH * d.Lp * d.Dp / 2;
+  out->qk_scale_bytes = BH * d.NB * 4;
+  out->qk_flag_bytes = BH * d.NB;
+  out->head_flag_bytes = BH * 4;
+  out->rope_bytes = BH * p->L * p->D * 2;
+  out->v_codes_bytes = BH * d.NB * p->D * 32;
+  out->v_scale_bytes = BH * p->D * 4;
+  out->v_colsum_bytes = BH * d.NB * p->D * 4;
+  out->out_min_elems = (p->L == 0) ? 0
+      : (int64_t)(p->B - 1) * p->stride_b + (int64_t)(p->H - 1) * p->stride_h + (int64_t)(p->L - 1) * p->stride_l + p->D;
+  return ROTATTN_OK;
+}
+
+int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (bytes == nullptr || call < 0 || call > ROTATTN_CALL_DEBUG_DUMP) return ROTATTN_EINVAL;
+  *bytes = layout(p, d, call).total;
+  return ROTATTN_OK;
+}
+
+int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k, const rotattn_qk_buffers* out,
+                        void* workspace, size_t workspace_bytes, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (q == nullptr || k == nullptr) return ROTATTN_EINVAL;
+  if ((rc = check_qk(out)) != ROTATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k)) return ROTATTN_EALIGN;
+  const Layout L = layout(p, d, ROTATTN_CALL_QUANTIZE_QK);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* tab = at<float>(workspace, L.tab);
+  rc = launched(launch_rope_tables(d.kp, tab, out->head_kflag, p->B * p->H, s));
+  if (rc != ROTATTN_OK) return rc;
+  QKOut o;
+  o.q_codes = out->q_codes; o.k_codes = out->k_codes;
+  o.q_scale = out->q_scale; o.k_scale = out->k_scale;
+  o.q_flag = out->q_flag; o.k_flag = out->k_flag;
+  o.head_kflag = out->head_kflag;
+  o.q_rope = static_cast<__half*>(out->q_rope);
+  o.k_rope = static_cast<__half*>(out->k_rope);
+  return launched(launch_qk_prologue(d.kp, static_cast<const __half*>(q), static_cast<const __half*>(k), tab, o, s));
+}
+
+int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_buffers* out, void* workspace,
+                       size_t workspace_bytes, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (v == nullptr) return ROTATTN_EINVAL;
+  if ((rc = check_v(out)) != ROTATTN_OK) return rc;
+  if (!aligned16(v)) return ROTATTN_EALIGN;
+  const Layout L = layout(p, d, ROTATTN_CALL_QUANTIZE_V);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;
+  VOut o{out->v_codes, out->v_scale, out->v_colsum};
+  return launched(launch_vquant(d.kp, static_cast<const __half*>(v), at<uint32_t>(workspace, L.absmax), o,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
+                      const void* v, const uint8_t* head_fallback, void* out, void* workspace,
+                      size_t workspace_bytes, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
+  if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
+  if ((rc = check_attention_args(p, qk, v, head_fallback, out)) != ROTATTN_OK) return rc;
+  const Layout L = layout(p, d, ROTATTN_CALL_ATTENTION);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;
+  return attention_impl(p, d, qk, vq, v, head_fallback, out, workspace, L, static_cast<hipStream_t>(stream));
+}
+
+int rotattn_forward(const rotattn_problem* p, const rotattn_qk_buffers* qk, const void* v,
+                    const uint8_t* head_fallback, void* out, void* workspace, size_t workspace_bytes,
+                    rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
+  if (v == nullptr) return ROTATTN_EINVAL;
+  if (!aligned16(v)) return ROTATTN_EALIGN;
+  if ((rc = check_attention_args(p, qk, v, head_fallback, out)) != ROTATTN_OK) return rc;
+  const Layout L = layout(p, d, ROTATTN_CALL_FORWARD);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  VOut o{at<uint8_t>(workspace, L.vcodes), at<float>(workspace, L.vscale), at<int32_t>(workspace, L.vcolsum)};
+  rc = launched(launch_vquant(d.kp, static_cast<const __half*>(v), at<uint32_t>(workspace, L.absmax), o, s));
+  if (rc != ROTATTN_OK) return rc;
+  rotattn_v_buffers vq{o.v_codes, o.v_scale, o.v_colsum};
+  return attention_impl(p, d, qk, &vq, v, head_fallback, out, workspace, L, s);
+}
+
+int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k, const void* v, void* out,
+                         void* workspace, size_t workspace_bytes, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return ROTATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ROTATTN_EALIGN;
+  const Layout L = layout(p, d, ROTATTN_CALL_FP16_FORWARD);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* tab = at<float>(workspace, L.tab);
+  __half* qr = at<__half>(workspace, L.qr);
+  __half* kr = at<__half>(workspace, L.kr);
+  if ((rc = launched(launch_rope_tables(d.kp, tab, nullptr, 0, s))) != ROTATTN_OK) return rc;
+  if ((rc = launched(launch_rope_copy(d.kp, static_cast<const __half*>(q), tab, qr, s))) != ROTATTN_OK) return rc;
+  if ((rc = launched(launch_rope_copy(d.kp, static_cast<const __half*>(k), tab, kr, s))) != ROTATTN_OK) return rc;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_rope = qr; a.k_rope = kr;
+  a.v = static_cast<const __half*>(v);
+  a.out = static_cast<__half*>(out);
+  a.route = false;
+  return launched(launch_fp16_attention(d.kp, a, true, s));
+}
+
+int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
+                       const uint8_t* head_fallback, const int32_t* units, int32_t n_units, int32_t* acc_qk,
+                       int8_t* p_codes, int32_t* acc_pv, float* m_hist, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
+  if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
+  if (n_units < 0 || (n_units > 0 && (!units || !acc_qk || !p_codes || !acc_pv || !m_hist))) return ROTATTN_EINVAL;
+  if (n_units == 0 || p->L == 0) return ROTATTN_OK;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_codes = qk->q_codes; a.k_codes = qk->k_codes;
+  a.q_scale = qk->q_scale; a.k_scale = qk->k_scale;
+  a.q_flag = qk->q_flag; a.k_flag = qk->k_flag; a.head_kflag = qk->head_kflag;
+  a.head_mask = head_fallback;
+  a.v_codes = vq->v_codes; a.v_scale = vq->v_scale;
+  a.route = routes(p);
+  a.units = units; a.n_units = n_units;
+  a.d_acc = acc_qk; a.d_pq = p_codes; a.d_pv = acc_pv; a.d_m = m_hist;
+  return launched(launch_int4_attention(d.kp, a, true, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

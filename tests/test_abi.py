@@ -1,0 +1,136 @@
+"""The C ABI on the host (no GPU): exports, sizes and every validation error, all decided before any launch."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+import workloads as W
+
+R = pytest.importorskip("int4_quantized_flashattention_amd")
+from int4_quantized_flashattention_amd import binding as Bd  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    try:
+        return Bd.load_library()
+    except RuntimeError as e:
+        pytest.skip(str(e))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "rotattn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(rotattn_\w+)\(", src, flags=re.M)))
+
+
+def test_exports_match_header():
+    lib = _lib()
+    names = _header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(Bd.EXPORTS) == names
+
+
+def test_version_and_strerror():
+    lib = _lib()
+    assert lib.rotattn_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.rotattn_strerror(code)
+
+
+def _p(**kw):
+    w = W.WORKLOADS["tiny"]
+    p = Bd.problem_from_workload(w)
+    for k, v in kw.items():
+        if k == "rope_split":
+            p.rope_split[0], p.rope_split[1], p.rope_split[2] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+def test_sizes_720p():
+    _lib()
+    p = Bd.problem_from_workload(W.WORKLOADS["720p"])
+    s = Bd.get_sizes(p)
+    assert (s.Lp, s.NB, s.Dp) == (75648, 1182, 128)
+    assert s.qk_codes_bytes == 40 * 75648 * 64
+    assert s.v_codes_bytes == 40 * 1182 * 128 * 32
+    assert s.v_colsum_bytes == 40 * 1182 * 128 * 4
+    p2 = Bd.problem_from_workload(W.WORKLOADS["480p"])
+    assert Bd.get_sizes(p2).Dp == 192
+    # partial buffers only when block routing is on
+    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == 0
+    assert Bd.workspace_bytes(Bd.problem_from_workload(W.WORKLOADS["mixed"]), Bd.CALL_ATTENTION) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), -2),
+    (dict(D=64), -1),                      # split no longer sums to D
+    (dict(rope_split=(40, 42, 42)), -1),
+    (dict(L=255), -1),                     # L != prefix + T*Hh*W
+    (dict(B=0), -1),
+    (dict(rotation=7), -1),
+    (dict(stride_l=100), -1),              # stride_l < D
+    (dict(stride_l=132), -3),              # rows not 16-byte aligned
+    (dict(rope_base=-1.0), -1),
+    (dict(block_err_tau=float("nan")), -1),
+    (dict(rotation=1, rope_split=(100, 14, 14)), -2),
+])
+def test_problem_validation(kw, code):
+    _lib()
+    p = _p(**kw)
+    s = Bd.Sizes()
+    assert Bd.load_library().rotattn_get_sizes(C.byref(p), C.byref(s)) == code
+
+
+def test_call_validation_before_launch():
+    """Null, misaligned and short-workspace arguments are rejected on the host (fake addresses are never touched)."""
+    lib = _lib()
+    p = _p()
+    good = 0x10000
+    qk = Bd.QKBuffers(*([good] * 7 + [None, None]))
+    stream = C.c_void_p(None)
+    n = Bd.workspace_bytes(p, Bd.CALL_QUANTIZE_QK)
+    assert n > 0
+    # null q
+    assert lib.rotattn_quantize_qk(C.byref(p), None, C.c_void_p(good), C.byref(qk), C.c_void_p(good), n, stream) == -1
+    # misaligned k
+    assert lib.rotattn_quantize_qk(C.byref(p), C.c_void_p(good), C.c_void_p(good + 2), C.byref(qk),
+                                   C.c_void_p(good), n, stream) == -3
+    # short workspace
+    assert lib.rotattn_quantize_qk(C.byref(p), C.c_void_p(good), C.c_void_p(good), C.byref(qk),
+                                   C.c_void_p(good), n - 1, stream) == -4
+    # missing code buffer
+    bad = Bd.QKBuffers(*([good] * 6 + [None, None, None]))
+    assert lib.rotattn_quantize_qk(C.byref(p), C.c_void_p(good), C.c_void_p(good), C.byref(bad),
+                                   C.c_void_p(good), n, stream) == -1
+    # the FP16 path needs the RoPE'd copies when routing is possible
+    vb = Bd.VBuffers(good, good, good)
+    mask = C.c_void_p(good)
+    assert lib.rotattn_attention(C.byref(p), C.byref(qk), C.byref(vb), C.c_void_p(good), mask, C.c_void_p(good),
+                                 None, 0, stream) == -1
+    # out missing
+    assert lib.rotattn_forward(C.byref(p), C.byref(qk), C.c_void_p(good), None, None, None, 0, stream) == -1
+    # fp16 forward without workspace
+    assert lib.rotattn_fp16_forward(C.byref(p), C.c_void_p(good), C.c_void_p(good), C.c_void_p(good),
+                                    C.c_void_p(good), None, 0, stream) == -4
+    # dump with a negative unit count
+    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, -1, None, None, None, None,
+                                  stream) == -1
+
+
+def test_empty_problem_is_a_no_op():
+    """L = 0 (no tokens) validates and enqueues nothing."""
+    lib = _lib()
+    p = _p(L=0, grid_t=0, text_prefix=0)
+    good = 0x10000
+    qk = Bd.QKBuffers(*([good] * 7 + [None, None]))
+    ws = C.c_void_p(0x100000)
+    n = Bd.workspace_bytes(p, Bd.CALL_QUANTIZE_QK)
+    assert lib.rotattn_quantize_qk(C.byref(p), C.c_void_p(good), C.c_void_p(good), C.byref(qk), ws, n,
+                                   C.c_void_p(None)) == 0

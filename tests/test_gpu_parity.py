@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Bars (bit-exact for integers, the stated tolerance for floating point):
+  Q/K/V codes, scales, column sums, int32 Q.K^T and P.V accumulators: bitwise;
+  block flags: exact except where the block's NSR is within 1e-4 of tau;
+  P codes: identical except +-1 where 15 P is within 1e-5 of a rounding
+  boundary, on at most 1e-4 of the entries; P.V accumulators compared on the
+  rows whose P codes all match; running max: bitwise;
+  outputs: |gpu - oracle| <= 2e-3 + 2^-10 |oracle| (quantized path), plus the
+  fp16 weight-rounding bound for tiles on the FP16 path.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import core as O
+from tests import gpu_common as G
+
+torch = G.torch
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, heads to check)
+    "tiny": W.WORKLOADS["tiny"],
+    "ragged_prefix": W.WORKLOADS["tiny"].replace(grid=(2, 5, 19), prefix=8),
+    "group64": W.WORKLOADS["480p"].replace(H=2, grid=(2, 7, 23)),
+    "d64_prefix": W.WORKLOADS["smalld"].replace(H=3, grid=(2, 5, 11)),
+    "d64_group64": W.WORKLOADS["smalld"].replace(H=2, grid=(1, 3, 30), prefix=5, rotation=W.ROT_GROUP64),
+    "lognormal": W.WORKLOADS["720p"].replace(H=2, grid=(3, 9, 16)),
+    "mixed": W.WORKLOADS["mixed"].replace(H=4, grid=(2, 9, 20)),
+}
+
+_cache = {}
+
+
+def _run(name):
+    """Run quantize_qk + quantize_v + forward + dump of every query block for a case (cached)."""
+    if name in _cache:
+        return _cache[name]
+    G.require_gpu()
+    w = CASES[name]
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    mask_np = W.head_fallback_mask(w)
+    mask = G.dev(mask_np) if mask_np is not None else None
+    need_rope = mask is not None or np.isfinite(w.tau)
+    print(f"[gpu] case={name} L={w.L} H={w.H} D={w.D} rot={w.rotation}", flush=True)
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    vq = G.R.rotattn_quantize_v(p, v)
+    out = G.R.rotattn_forward(p, qk, v, head_fallback=mask)
+    s = G.R.get_sizes(p)
+    units = np.arange(w.B * w.H * s.NB, dtype=np.int32)
+    dump = G.R.rotattn_debug_dump(p, qk, vq, G.dev(units), head_fallback=mask)
+    torch.cuda.synchronize()
+    res = {
+        "w": w, "x": x, "p": p, "mask": mask_np, "need_rope": need_rope, "NB": s.NB, "Lp": s.Lp,
+        "q_codes": G.unpack_qk_codes(G.host(qk.q_codes)), "k_codes": G.unpack_qk_codes(G.host(qk.k_codes)),
+        "q_scale": G.host(qk.q_scale), "k_scale": G.host(qk.k_scale),
+        "q_flag": G.host(qk.q_flag), "k_flag": G.host(qk.k_flag), "head_kflag": G.host(qk.head_kflag),
+        "q_rope": G.host(qk.q_rope), "k_rope": G.host(qk.k_rope),
+        "v_codes": G.decode_v_codes(G.host(vq.v_codes)), "v_scale": G.host(vq.v_scale),
+        "v_colsum": G.host(vq.v_colsum), "out": G.host(out).astype(np.float64),
+        "dump": {kk: G.host(t) for kk, t in dump.items()},
+    }
+    res["oracle"] = {}
+    for b in range(w.B):
+        for h in range(w.H):
+            masked = bool(mask_np[b * w.H + h]) if mask_np is not None else False
+            # follow the GPU's block flags where the oracle agrees up to the threshold tolerance
+            o = G.oracle_head(w, x, b, h, head_masked=masked)
+            qf = res["q_flag"][b, h].astype(bool)
+            kf = res["k_flag"][b, h].astype(bool)
+            if not (np.array_equal(qf, o["q_flags"]) and np.array_equal(kf, o["k_flags"])):
+                o = G.oracle_head(w, x, b, h, head_masked=masked, q_flags=qf, k_flags=kf)
+            res["oracle"][(b, h)] = o
+    _cache[name] = res
+    return res
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prologue_parity(name):
+    r = _run(name)
+    w = r["w"]
+    for (b, h), o in r["oracle"].items():
+        for t in ("q", "k"):
+            assert np.array_equal(r[f"{t}_codes"][b, h], o[t]["codes"]), (t, b, h)
+            assert np.array_equal(r[f"{t}_scale"][b, h], o[t]["scale"]), (t, b, h)
+            assert G.flags_agree(r[f"{t}_flag"][b, h], o[t]["nsr"], w.tau), (t, b, h)
+            assert np.array_equal(r[f"{t}_rope"][b, h], o[t]["rope16"]), (t, b, h)
+        assert bool(r["head_kflag"][b * w.H + h]) == bool(r["k_flag"][b, h].any())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_vquant_parity(name):
+    r = _run(name)
+    for (b, h), o in r["oracle"].items():
+        assert np.array_equal(r["v_codes"][b, h], o["v_codes"]), (b, h)
+        assert np.array_equal(r["v_scale"][b, h], o["v_scale"]), (b, h)
+        assert np.array_equal(r["v_colsum"][b, h], o["v_colsum"]), (b, h)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_int4_loop_parity(name):
+    """Dump of the INT4 kernel (every query block) against the oracle's loop on the same codes and routing."""
+    r = _run(name)
+    w, NB, L = r["w"], r["NB"], r["w"].L
+    d = r["dump"]
+    total = mism = 0
+    for (b, h), o in r["oracle"].items():
+        masked = r["mask"] is not None and r["mask"][b * w.H + h]
+        qf, kf = o["q_flags"], o["k_flags"]
+        for qb in range(NB):
+            if masked or qf[qb]:
+                continue
+            u = (b * w.H + h) * NB + qb
+            rows = np.arange(qb * 64, min(qb * 64 + 64, L))
+            ref = O.int4_flash_rows(o["q"]["codes"], o["q"]["scale"], o["k"]["codes"], o["k"]["scale"],
+                                    o["v_codes"], o["v_scale"], o["v_colsum"], L, w.D, rows,
+                                    key_blocks=~kf, dump=True)
+            n = rows.size
+            keep = np.repeat(~kf, 64)[:L]
+            assert np.array_equal(d["acc"][u, :n, :L][:, keep], ref["acc"][:, :L][:, keep]), (b, h, qb)
+            mh = d["m"][u, :n]
+            assert np.array_equal(mh[:, ~kf], ref["m_hist"][:, ~kf]), (b, h, qb)
+            # oracle P for the tie check
+            gp = d["pq"][u, :n, :L][:, keep]
+            op = ref["pq"][:, :L][:, keep]
+            acc = ref["acc"][:, :L][:, keep].astype(np.float32)
+            cq = np.float32(o["q"]["scale"][qb] * O.softmax_c0(w.D))
+            kidx = np.nonzero(keep)[0]
+            c = (cq * o["k"]["scale"][kidx // 64]).astype(np.float32)
+            S2 = (acc * c[None, :]).astype(np.float32)
+            mrow = ref["m_hist"][:, kidx // 64]
+            P = np.exp2((S2 - mrow).astype(np.float32).astype(np.float64)).astype(np.float32)
+            ok, nb = G.tie_mismatch_ok(gp, op, P)
+            assert ok, (b, h, qb, nb)
+            total += gp.size
+            mism += nb
+            same_rows = np.all(gp == op, axis=1)
+            pv = d["accpv"][u, :n][same_rows][:, ~kf]
+            assert np.array_equal(pv, ref["accpv"][same_rows][:, ~kf]), (b, h, qb)
+    assert mism <= 1e-4 * max(total, 1), (mism, total)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_parity(name):
+    """Final fp16 output of rotattn_forward against the oracle (rows with a P-code tie flip are set aside)."""
+    r = _run(name)
+    w, NB, L = r["w"], r["NB"], r["w"].L
+    d = r["dump"]
+    flipped = 0
+    for (b, h), o in r["oracle"].items():
+        ref = o["out"]
+        got = r["out"][b, h]
+        tol = G.ATOL + G.RTOL * np.abs(ref)
+        # rows with any FP16 tile: add the fp16 weight-rounding bound
+        masked = r["mask"] is not None and r["mask"][b * w.H + h]
+        qf, kf = o["q_flags"], o["k_flags"]
+        rows_all = np.arange(L)
+        fp16_rows = masked | qf[rows_all // 64]
+        if fp16_rows.any():
+            rr = rows_all[fp16_rows]
+            _, bound = G.fp16_weight_bound(o["q"]["rope16"], o["k"]["rope16"], r["x"]["v"][b, h], L, w.D, rr)
+            tol[rr] += bound
+        if kf.any():
+            rr = rows_all[~fp16_rows]
+            p2, bound = G.fp16_weight_bound(o["q"]["rope16"], o["k"]["rope16"], r["x"]["v"][b, h], L, w.D, rr,
+                                            key_blocks=kf)
+            tol[rr] += bound
+        # rows whose P codes differ from the oracle's at a tie
+        flip = np.zeros(L, bool)
+        for qb in range(NB):
+            if masked or qf[qb]:
+                continue
+            u = (b * w.H + h) * NB + qb
+            rows = np.arange(qb * 64, min(qb * 64 + 64, L))
+            ref_pq = O.int4_flash_rows(o["q"]["codes"], o["q"]["scale"], o["k"]["codes"], o["k"]["scale"],
+                                       o["v_codes"], o["v_scale"], o["v_colsum"], L, w.D, rows,
+                                       key_blocks=~kf, dump=True)["pq"]
+            keep = np.repeat(~kf, 64)[:L]
+            flip[rows] = np.any(d["pq"][u, :rows.size, :L][:, keep] != ref_pq[:, :L][:, keep], axis=1)
+        flipped += int(flip.sum())
+        ok = np.abs(got - ref) <= tol
+        assert ok[~flip].all(), (b, h, np.abs(got - ref)[~flip].max(), np.argwhere(~ok & ~flip)[:5])
+    assert flipped <= max(1, 0.01 * w.B * w.H * L)
+
+
+@pytest.mark.parametrize("name", ["tiny", "d64_prefix", "ragged_prefix"])
+def test_fp16_forward_parity(name):
+    """Whole-call FP16 path (RoPE, no rotation or quantization) against exact float64 attention on the fp16-rounded RoPE'd inputs."""
+    G.require_gpu()
+    w = CASES[name]
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    out = G.host(G.R.rotattn_fp16_forward(p, G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"]))).astype(np.float64)
+    for b in range(w.B):
+        for h in range(w.H):
+            qr = O.apply_rope(x["q"][b, h].astype(np.float32), w.prefix, w.grid, w.split, w.base).astype(np.float16)
+            kr = O.apply_rope(x["k"][b, h].astype(np.float32), w.prefix, w.grid, w.split, w.base).astype(np.float16)
+            rows = np.arange(w.L)
+            pp, bound = G.fp16_weight_bound(qr, kr, x["v"][b, h], w.L, w.D, rows)
+            ref = pp["O"] / pp["l"][:, None]
+            tol = G.ATOL + G.RTOL * np.abs(ref) + bound
+            assert (np.abs(out[b, h] - ref) <= tol).all(), (b, h, np.abs(out[b, h] - ref).max())
+
+
+def test_all_heads_masked_equals_fp16_forward():
+    """A head mask of all ones routes every tile to FP16: identical bits to the whole-call FP16 forward."""
+    G.require_gpu()
+    w = CASES["ragged_prefix"]
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    mask = torch.ones(w.B * w.H, dtype=torch.uint8, device="cuda")
+    a = G.host(G.R.rotattn_forward(p, qk, v, head_fallback=mask))
+    bb = G.host(G.R.rotattn_fp16_forward(p, q, k, v))
+    assert np.array_equal(a.view(np.uint16), bb.view(np.uint16))
+
+
+def test_determinism():
+    """Two runs give bitwise-equal outputs and dumps."""
+    G.require_gpu()
+    w = CASES["mixed"]
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    mask = G.dev(W.head_fallback_mask(w))
+    outs = []
+    for _ in range(2):
+        qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+        outs.append(G.host(G.R.rotattn_forward(p, qk, v, head_fallback=mask)).view(np.uint16))
+    assert np.array_equal(outs[0], outs[1])
