@@ -28,23 +28,48 @@
 #include "common.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace rotattn {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int DP, int DV, bool DUMP>
-__global__ __launch_bounds__(256) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0) {
-  constexpr int NC = DP / 32;            // 32-deep slices of the rotated head dim
-  constexpr int NCT = DV / 32;           // 32-channel output tiles
-  constexpr int KT_BYTES = kBlock * DP / 2;
-  constexpr int VT_BYTES = DV * 32;
-  constexpr int QROW = DP / 2;           // code bytes per token
-  constexpr int HALF = DP / 4;           // code bytes of one lane half
-  __shared__ __attribute__((aligned(16))) uint8_t ks[KT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[VT_BYTES];
+// Unpacks 16 packed bytes (32 INT4 codes) into 32 int8 bytes (each code times
+// 16) in the order the matrix-core operands read them, and stores them to LDS.
+__device__ __forceinline__ void store_unpacked(uint8_t* dst, uint4 p) {
+  uint4 a, b;
+  a.x = nib_lo16(p.x); a.y = nib_hi16(p.x); a.z = nib_lo16(p.y); a.w = nib_hi16(p.y);
+  b.x = nib_lo16(p.z); b.y = nib_hi16(p.z); b.z = nib_lo16(p.w); b.w = nib_hi16(p.w);
+  reinterpret_cast<uint4*>(dst)[0] = a;
+  reinterpret_cast<uint4*>(dst)[1] = b;
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
+// 64: the packed K and V codes (prefetched into registers during the previous
+// block) are unpacked once into one of two LDS stages, one barrier, then every
+// wave runs two S^T tiles, the online softmax and four O^T tiles on the
+// matrix cores. O is accumulated in int32 by the matrix cores and folded into
+// the float32 accumulator only when some row max of the wave grows (the
+// rescale factor is exactly 1 otherwise).
+template <int DP, int DV, int NW, bool DUMP>
+__global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
+  constexpr int NT = NW * 64;
+  constexpr int NC = DP / 32;              // 32-deep slices of the rotated head dim
+  constexpr int NCT = DV / 32;             // 32-channel output tiles
+  constexpr int QROW = DP / 2;             // packed code bytes per token
+  constexpr int HALF = DP / 4;             // packed code bytes of one lane half
+  constexpr int KPK = kBlock * DP / 2;     // packed K bytes per key block
+  constexpr int VPK = DV * 32;             // packed V bytes per key block
+  constexpr int PK = KPK + VPK;
+  constexpr int KROW = DP + 16;            // unpacked K row in LDS (padded)
+  constexpr int VROW = 64 + 16;            // unpacked V channel row in LDS (padded)
+  constexpr int KST = kBlock * KROW;
+  constexpr int STAGE = KST + DV * VROW + 16;   // + the K block scale
+  constexpr int NLOAD = (PK + NT * 16 - 1) / (NT * 16);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
   const int L = kp.L, Lp = kp.Lp, NB = kp.NB;
 
@@ -60,7 +85,7 @@ __global__ __launch_bounds__(256) void int4_attn_kernel(KProblem kp, AttnArgs a,
   } else {
     b = blockIdx.z;
     h = blockIdx.y;
-    row_base = blockIdx.x * 128;
+    row_base = blockIdx.x * (32 * NW);
   }
   const int bh = b * kp.H + h;
   const int wrow = row_base + 32 * wave;
@@ -84,126 +109,184 @@ __global__ __launch_bounds__(256) void int4_attn_kernel(KProblem kp, AttnArgs a,
     cq = fmul_rn(a.q_scale[bh * NB + qblk], c0);
   }
 
+  const uint8_t* kg = a.k_codes + (long long)bh * Lp * QROW;
+  const uint8_t* vg = a.v_codes + (long long)bh * NB * VPK;
+  const uint8_t* kflag = a.route ? a.k_flag + (long long)bh * NB : nullptr;
+  auto next_block = [&](int j) {
+    if (kflag != nullptr)
+      while (j < NB && kflag[j] != 0) ++j;   // FP16 tile: the other path takes it
+    return j;
+  };
+  uint4 pre[NLOAD];
+  float sk_next = 0.f;   // K block scale, carried through LDS with the tile
+  auto load_block = [&](int j) {
+    if (tid == 0) sk_next = a.k_scale[bh * NB + j];
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int o = (tid + i * NT) * 16;
+      if (o < KPK) pre[i] = *reinterpret_cast<const uint4*>(kg + (long long)j * KPK + o);
+      else if (o < PK) pre[i] = *reinterpret_cast<const uint4*>(vg + (long long)j * VPK + (o - KPK));
+    }
+  };
+  auto store_block = [&](int stage) {
+    uint8_t* base = smem + stage * STAGE;
+    if (tid == 0) *reinterpret_cast<float*>(base + STAGE - 16) = sk_next;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      const int o = (tid + i * NT) * 16;
+      if (o < KPK) {
+        const int r = o / QROW, bo = o - (o / QROW) * QROW;
+        store_unpacked(base + r * KROW + 2 * bo, pre[i]);
+      } else if (o < PK) {
+        const int ov = o - KPK, c = ov >> 5, bo = ov & 31;
+        store_unpacked(base + KST + c * VROW + 2 * bo, pre[i]);
+      }
+    }
+  };
+
   float m_run = -INFINITY;
-  float l_part = 0.f;
-  v16f o_acc[NCT];
+  float l15 = 0.f;                 // row sum of 15 P (lane-partial)
+  v16f o_acc[NCT];                 // float32 O (times 16), flushed from pacc
+  v16i pacc[NCT];                  // int32 O (times 16) since the last flush
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o_acc[ct][v] = 0.f;
+    for (int v = 0; v < 16; ++v) { o_acc[ct][v] = 0.f; pacc[ct][v] = 0; }
 
-  const uint8_t* kbase_g = a.k_codes + (long long)bh * Lp * QROW;
-  const uint8_t* vbase_g = a.v_codes + (long long)bh * NB * VT_BYTES;
-
-  for (int j = 0; j < NB; ++j) {
-    if (a.route && a.k_flag[bh * NB + j] != 0) continue;   // FP16 tile: the other path takes it
-    __syncthreads();
-    {
-      const uint8_t* kt = kbase_g + (long long)j * KT_BYTES;
-      for (int o = threadIdx.x * 16; o < KT_BYTES; o += 256 * 16)
-        *reinterpret_cast<uint4*>(ks + o) = *reinterpret_cast<const uint4*>(kt + o);
-      const uint8_t* vt = vbase_g + (long long)j * VT_BYTES;
-      for (int o = threadIdx.x * 16; o < VT_BYTES; o += 256 * 16)
-        *reinterpret_cast<uint4*>(vs + o) = *reinterpret_cast<const uint4*>(vt + o);
-    }
-    __syncthreads();
-    if (!work) continue;
-
-    // S^T tile (times 256): two 32-key halves of the block.
-    v16i sacc[2];
+  auto block_step = [&](auto ragged_tag, int stage, int j) {
+    constexpr bool kRagged = decltype(ragged_tag)::value;
+      const uint8_t* Ks = smem + stage * STAGE;
+      const uint8_t* Vs = Ks + KST;
+      // S^T (times 256) for the two 32-key halves of the block
+      v16i s0, s1;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[s][v] = 0;
-      const uint8_t* krow = ks + (32 * s + col) * QROW + hh * HALF;
+      for (int v = 0; v < 16; ++v) { s0[v] = 0; s1[v] = 0; }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const v4i kop = unpack16(*reinterpret_cast<const uint2*>(krow + 8 * c));
-        sacc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[c], sacc[s], 0, 0, 0);
+        const v4i a0 = *reinterpret_cast<const v4i*>(Ks + col * KROW + hh * (DP / 2) + 16 * c);
+        const v4i a1 = *reinterpret_cast<const v4i*>(Ks + (32 + col) * KROW + hh * (DP / 2) + 16 * c);
+        s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qop[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qop[c], s1, 0, 0, 0);
       }
-    }
-    // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly.
-    const float ct_scale = fmul_rn(fmul_rn(cq, a.k_scale[bh * NB + j]), 1.0f / 256.0f);
-    const int key0 = j * kBlock;
-    int mx = INT_MIN;
+      // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly
+      const float sk = *reinterpret_cast<const float*>(Ks + STAGE - 16);
+      const float cs = fmul_rn(fmul_rn(cq, sk), 1.0f / 256.0f);
+      const int key0 = j * kBlock;
+      int mx;
+      if (!kRagged) {
+        mx = max(s0[0], s1[0]);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+        for (int v = 1; v < 16; ++v) mx = max(mx, max(s0[v], s1[v]));
+      } else {
+        mx = INT_MIN;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (key < L) mx = max(mx, sacc[s][v]);
+        for (int v = 0; v < 16; ++v) {
+          const int k0 = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (k0 < L) mx = max(mx, s0[v]);
+          if (k0 + 32 < L) mx = max(mx, s1[v]);
+        }
       }
-    mx = max(mx, __shfl_xor(mx, 32));
-    // max over the block of float(acc) * c = float(max acc) * c, as c >= 0
-    const float m_blk = fmul_rn((float)mx, ct_scale);
-    const float m_new = fmaxf(m_run, m_blk);
-    const float alpha = exp2_hw(fsub_rn(m_run, m_new));
-
-    v4i pop[2];
-    float psum = 0.f;
+      mx = max(mx, __shfl_xor(mx, 32));
+      // max over the block of float(acc) * c = float(max acc) * c, as c >= 0
+      const float m_new = fmaxf(m_run, fmul_rn((float)mx, cs));
+      if (DUMP || __ballot(m_new > m_run) != 0ull) {
+        const float alpha = exp2_hw(fsub_rn(m_run, m_new));
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        uint32_t word = 0;
+          for (int v = 0; v < 16; ++v) {
+            // everything accumulated so far (float and pending int32) is at the old max
+            o_acc[ct][v] = alpha * (o_acc[ct][v] + (float)pacc[ct][v]);
+            pacc[ct][v] = 0;
+          }
+        l15 *= alpha;
+        m_run = m_new;
+      }
+      // 15 P = 2^(acc c - (m - log2 15)); its rne is pq + 8, packed by v_cvt_pk_u8_f32
+      const float nm15 = -fsub_rn(m_run, log2_15);
+      v4i pop[2];
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int v = 4 * kq + bb;
-          const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
-          float P = 0.f;
-          if (key < L) P = exp2_hw(fsub_rn(fmul_rn((float)sacc[s][v], ct_scale), m_new));
-          psum += P;
-          const uint32_t code = (uint32_t)(int)rintf(fmul_rn(15.0f, P));   // pq + 8 in [0, 15]
-          word |= code << (8 * bb);
-          if (DUMP) {
-            const int r = 32 * wave + col;
-            if (wrow + col < L) {
-              const long long di = ((long long)unit_idx * kBlock + r) * Lp + key;
-              a.d_acc[di] = sacc[s][v] >> 8;
-              a.d_pq[di] = (int8_t)((int)code - 8);
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int v = 4 * kq + bb;
+            float t = fmaf((float)(s == 0 ? s0[v] : s1[v]), cs, nm15);
+            if (kRagged) {
+              const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
+              if (key >= L) t = -INFINITY;
+            }
+            const float p15 = exp2_hw(t);
+            if (bb & 1) ls1 += p15; else ls0 += p15;
+            word = __builtin_amdgcn_cvt_pk_u8_f32(p15, bb, word);
+            if (DUMP && wrow + col < L) {
+              const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
+              const long long di = ((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key;
+              a.d_acc[di] = (s == 0 ? s0[v] : s1[v]) >> 8;
+              a.d_pq[di] = (int8_t)((int)((word >> (8 * bb)) & 0xFFu) - 8);
             }
           }
+          pop[s][kq] = (int)word;
         }
-        pop[s][kq] = (int)word;
+      l15 += ls0 + ls1;
+      // O^T += V^T (pq + 8)^T: the zero-point correction rides inside the product
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const v4i vop = *reinterpret_cast<const v4i*>(Vs + (ct * 32 + col) * VROW + 32 * hh + 16 * s);
+          pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pop[s], pacc[ct], 0, 0, 0);
+        }
       }
-    l_part = alpha * l_part + psum;
-
+      if (DUMP && wrow + col < L) {
+        const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      v16i pacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) pacc[v] = 0;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint8_t* vrow = vs + (ct * 32 + col) * 32 + 16 * hh + 8 * s;
-        const v4i vop = unpack16(*reinterpret_cast<const uint2*>(vrow));
-        pacc = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pop[s], pacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o_acc[ct][v] = alpha * o_acc[ct][v] + (float)pacc[v];
-      if (DUMP) {
-        const int r = 32 * wave + col;
-        if (wrow + col < L) {
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int ch = ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            a.d_pv[(((long long)unit_idx * kBlock + r) * NB + j) * DV + ch] = pacc[v] >> 4;
+            a.d_pv[(r * NB + j) * DV + ch] = pacc[ct][v] >> 4;
           }
-        }
+        if (hh == 0) a.d_m[r * NB + j] = m_run;
       }
-    }
-    m_run = m_new;
-    if (DUMP && hh == 0 && wrow + col < L)
-      a.d_m[((long long)unit_idx * kBlock + 32 * wave + col) * NB + j] = m_run;
+      };
+
+  // Full key blocks in the loop; the ragged last block (keys at or beyond L)
+  // after it, so that the hot loop carries no key mask.
+  const int nfull = L / kBlock;
+  int j = next_block(0);
+  if (j < NB) load_block(j);
+  int stage = 0;
+  while (j < nfull) {
+    store_block(stage);
+    __syncthreads();
+    const int jn = next_block(j + 1);
+    if (jn < NB) load_block(jn);
+    if (work) block_step(std::integral_constant<bool, false>(), stage, j);
+    stage ^= 1;
+    j = jn;
+  }
+  if (j < NB) {
+    store_block(stage);
+    __syncthreads();
+    if (work) block_step(std::integral_constant<bool, true>(), stage, j);
   }
 
   if (DUMP || !work) return;
-  const float l = l_part + __shfl_xor(l_part, 32);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o_acc[ct][v] += (float)pacc[ct][v];
+  const float l15t = l15 + __shfl_xor(l15, 32);
   const int row = wrow + col;
   if (row >= L) return;
   const float* svp = a.v_scale + (long long)bh * DV;
   if (!mixed) {
-    const float inv_l = 1.0f / l;
+    // out = O (s_v / 15) / l with O = o/16 and l = l15/15
+    const float inv = 1.0f / (16.0f * l15t);
     __half* orow = a.out + (long long)b * kp.sb + (long long)h * kp.sh + (long long)row * kp.sl;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -212,8 +295,7 @@ __global__ __launch_bounds__(256) void int4_attn_kernel(KProblem kp, AttnArgs a,
         const int ch = ct * 32 + 8 * g + 4 * hh;
         __half hv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          hv[e] = __float2half_rn(o_acc[ct][4 * g + e] * (svp[ch + e] * (1.0f / 240.0f)) * inv_l);
+        for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn(o_acc[ct][4 * g + e] * svp[ch + e] * inv);
         *reinterpret_cast<uint2*>(orow + ch) = *reinterpret_cast<const uint2*>(hv);
       }
   } else {
@@ -232,28 +314,37 @@ __global__ __launch_bounds__(256) void int4_attn_kernel(KProblem kp, AttnArgs a,
       }
     if (hh == 0) {
       a.part_m[(long long)bh * Lp + row] = m_run;
-      a.part_l[(long long)bh * Lp + row] = l;
+      a.part_l[(long long)bh * Lp + row] = l15t * (1.0f / 15.0f);
     }
   }
 }
 
+// waves per workgroup (32 query rows each): four, so that two independent
+// workgroups share a CU and one's softmax overlaps the other's matrix work
+template <int DP>
+constexpr int waves_for() { return 4; }
+
 template <int DP, int DV>
-static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump, float c0, hipStream_t s) {
+static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump, float c0, float l15,
+                                hipStream_t s) {
+  constexpr int kWaves = waves_for<DP>();
   if (dump) {
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, true>), dim3(a.n_units), dim3(256), 0, s, kp, a, c0);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, kWaves, true>), dim3(a.n_units), dim3(kWaves * 64), 0, s, kp, a,
+                       c0, l15);
   } else {
-    dim3 grid((kp.L + 127) / 128, kp.H, kp.B);
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, false>), grid, dim3(256), 0, s, kp, a, c0);
+    dim3 grid((kp.L + 32 * kWaves - 1) / (32 * kWaves), kp.H, kp.B);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, kWaves, false>), grid, dim3(kWaves * 64), 0, s, kp, a, c0, l15);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_int4_attention(const KProblem& kp, const AttnArgs& a, bool dump, hipStream_t s) {
   const float c0 = (float)(std::log2(2.718281828459045) / std::sqrt((double)kp.D));
-  if (kp.Dp == 128 && kp.D == 128) return launch_int4_t<128, 128>(kp, a, dump, c0, s);
-  if (kp.Dp == 192 && kp.D == 128) return launch_int4_t<192, 128>(kp, a, dump, c0, s);
-  if (kp.Dp == 64 && kp.D == 64) return launch_int4_t<64, 64>(kp, a, dump, c0, s);
-  if (kp.Dp == 192 && kp.D == 64) return launch_int4_t<192, 64>(kp, a, dump, c0, s);
+  const float l15 = (float)std::log2(15.0);
+  if (kp.Dp == 128 && kp.D == 128) return launch_int4_t<128, 128>(kp, a, dump, c0, l15, s);
+  if (kp.Dp == 192 && kp.D == 128) return launch_int4_t<192, 128>(kp, a, dump, c0, l15, s);
+  if (kp.Dp == 64 && kp.D == 64) return launch_int4_t<64, 64>(kp, a, dump, c0, l15, s);
+  if (kp.Dp == 192 && kp.D == 64) return launch_int4_t<192, 64>(kp, a, dump, c0, l15, s);
   return hipErrorInvalidValue;
 }
 

@@ -313,11 +313,15 @@ def softmax_c0(D: int) -> np.float32:
     return F32(math.log2(math.e) / math.sqrt(D))
 
 
+LOG2_15 = F32(math.log2(15.0))
+
+
 def p_codes(P32: np.ndarray) -> np.ndarray:
     """Range-optimized P quantization: pq = rne(float32(15 * P)) - 8.
 
     P = exp(S - max S) is in [0, 1]; the fixed scale 1/15 and zero-point -8
     send 0 to -8 and 1 to 7, the whole INT4 range (RotateAttention abstract).
+    (The flash loop evaluates the same map as rne(2 ** (t + log2 15)) - 8.)
     """
     return (np.rint(F32(15.0) * P32) - 8).astype(np.int8)
 
@@ -336,20 +340,25 @@ def int4_flash_rows(qc, sq, kc, sk, vc, sv, colsum, L: int, D: int, rows, key_bl
     exp -> exp2 and the scale folded into the log2 domain):
       acc   = q . k over the rotated dims                 (exact integer)
       c     = float32(float32(sq * c0) * sk[j])
-      S2    = float32(float32(acc) * c)                   (padded keys: -inf)
+      S2    = float32(acc * c)                            (padded keys: -inf)
       m'    = max(m, rowmax S2)                           (m starts at -inf)
-      P     = float32(2 ** float32(S2 - m'))              (in [0, 1])
-      pq    = rne(float32(15 P)) - 8                       (in [-8, 7])
-      l     = 2**(m - m') l + rowsum P                     (from float32 P)
-      accPV = pq . v + 8 * colsum[j]                       (exact integer)
+      P15   = float32(2 ** float32(acc * c - m15)),  m15 = float32(m' - float32(log2 15))
+              i.e. 15 P with P = 2 ** (S2 - m') in [0, 1]; the product acc*c
+              enters the subtraction unrounded (one rounding, a fused
+              multiply-add)
+      pq    = rne(P15) - 8                                (in [-8, 7])
+      l     = 2**(m - m') l + rowsum P                    (from the unquantized P)
+      accPV = pq . v + 8 * colsum[j]                      (exact integer)
       O     = 2**(m - m') O + accPV
     Final: O_scaled = O * s_v / 15 and out = O_scaled / l.
 
     Reading: the running max advances per key block of 64 keys in ascending
     order (the P codes depend on it), skipping blocks not in key_blocks; the
-    row sum l uses the unquantized P.
+    row sum l uses the unquantized P; the constant 15 of the P quantizer is
+    applied as log2(15) inside the exponent, which equals float32(15 * P)
+    except within a few float32 ulps of a rounding boundary.
 
-    With quantize_p=False the loop keeps P in float64 and accumulates
+    With quantize_p=False the loop keeps P unquantized and accumulates
     P . v directly (no codes, no colsum): the plain FlashAttention recurrence.
 
     Returns a dict with O_scaled [R, D] float64, m [R] (float32 values), l [R]
@@ -384,19 +393,22 @@ def int4_flash_rows(qc, sq, kc, sk, vc, sv, colsum, L: int, D: int, rows, key_bl
         valid = (np.arange(k0, k0 + BLOCK) < L)
         acc = Qf @ kk.T                                   # exact small integers (or reals)
         c = (cq * F32(sk[j])).astype(F32)
-        S2 = (acc.astype(F32) * c[:, None]).astype(F32)
+        exact = acc.astype(F32).astype(F64) * c.astype(F64)[:, None]   # float32(acc) * c, unrounded
+        S2 = exact.astype(F32)
         S2[:, ~valid] = -np.inf
         m_new = np.maximum(m, S2.max(axis=1)).astype(F32)
         alpha = np.exp2((m - m_new).astype(F64))          # -inf - finite -> -inf -> 0
-        t = (S2 - m_new[:, None]).astype(F32)
-        P = np.exp2(t.astype(F64)).astype(F32)
-        l = alpha * l + P.astype(F64).sum(axis=1)
+        m15 = (m_new - LOG2_15).astype(F32)
+        t15 = (exact - m15.astype(F64)[:, None]).astype(F32)
+        P15 = np.exp2(t15.astype(F64)).astype(F32)
+        P15[:, ~valid] = 0
+        l = alpha * l + P15.astype(F64).sum(axis=1) / 15.0
         vv = np.asarray(vc[k0:k0 + BLOCK], dtype=F64)
         if quantize_p:
-            pq = p_codes(P)
+            pq = (np.rint(P15) - 8).astype(np.int8)
             accpv = pq.astype(F64) @ vv + 8.0 * colsum[j].astype(F64)[None, :]
         else:
-            accpv = P.astype(F64) @ vv
+            accpv = (P15.astype(F64) / 15.0) @ vv
         O = alpha[:, None] * O + accpv
         m = m_new
         if dump:

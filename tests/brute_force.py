@@ -63,6 +63,10 @@ def coords_of(n: int, prefix: int, grid):
 def flash_brute(qc, sq, kc, sk, vc, sv, L: int, D: int, rows, key_blocks=None):
     """Per-row, per-key scalar loop of the INT4 flash recurrence (float32 scalars).
 
+    The exponent argument is float32(acc * c - m15) with the product kept
+    exact (Python float) and m15 = float32(m - float32(log2 15)); the P code is
+    rne(2 ** that) - 8, and the row sum adds 2 ** that / 15.
+
     Returns (out float64 [R, Dv], pq int [R, Lp]).
     """
     nb = (L + 63) // 64
@@ -83,28 +87,29 @@ def flash_brute(qc, sq, kc, sk, vc, sv, L: int, D: int, rows, key_blocks=None):
             if not key_blocks[j]:
                 continue
             c = F32(cq * F32(sk[j]))
-            s2 = []
+            exact = []
             for kk in range(64 * j, 64 * j + 64):
                 if kk >= L:
-                    s2.append(F32(-np.inf))
+                    exact.append(None)
                     continue
                 acc = 0
                 for d in range(Dq):
                     acc += int(qc[r, d]) * int(kc[kk, d])
-                s2.append(F32(F32(acc) * c))
-            mb = max(s2)
+                exact.append(float(F32(acc)) * float(c))
+            mb = max(F32(e) for e in exact if e is not None)
             m_new = F32(max(m, mb))
             alpha = 0.0 if m == -np.inf else 2.0 ** float(F32(m - m_new))
+            m15 = F32(m_new - F32(math.log2(15.0)))
             psum = 0.0
             accpv = [0] * Dv
             for t, kk in enumerate(range(64 * j, 64 * j + 64)):
-                if s2[t] == -np.inf:
-                    P = F32(0.0)
+                if exact[t] is None:
+                    P15 = F32(0.0)
                 else:
-                    P = F32(2.0 ** float(F32(s2[t] - m_new)))
-                q = int(np.rint(F32(F32(15.0) * P))) - 8
+                    P15 = F32(2.0 ** float(F32(exact[t] - float(m15))))
+                q = int(np.rint(P15)) - 8
                 pq_row[kk] = q
-                psum += float(P)
+                psum += float(P15) / 15.0
                 for c_ in range(Dv):
                     accpv[c_] += q * int(vc[kk, c_])
             for c_ in range(Dv):

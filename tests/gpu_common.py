@@ -112,7 +112,7 @@ def fp16_weight_bound(qr16, kr16, v16, L, D, rows, key_blocks=None):
     return p, 2.0 ** -11 * (P @ va) / p["l"][:, None] + 2.0 ** -25 * va.sum(0)[None, :] / p["l"][:, None]
 
 
-def tie_mismatch_ok(gpu_pq, oracle_pq, P_oracle, eps=1e-5):
+def tie_mismatch_ok(gpu_pq, oracle_pq, P15_oracle, eps=1e-5):
     """P codes may differ by 1 where 15 P sits within eps of a rounding boundary (the exp2 evaluations differ)."""
     diff = gpu_pq.astype(int) - oracle_pq.astype(int)
     bad = diff != 0
@@ -120,6 +120,6 @@ def tie_mismatch_ok(gpu_pq, oracle_pq, P_oracle, eps=1e-5):
         return True, 0
     if np.abs(diff[bad]).max() > 1:
         return False, int(bad.sum())
-    x = 15.0 * P_oracle[bad].astype(np.float64)
+    x = P15_oracle[bad].astype(np.float64)
     near = np.abs(x - np.floor(x) - 0.5) < eps
     return bool(near.all()), int(bad.sum())
