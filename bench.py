@@ -62,6 +62,8 @@ def main():
     ap.add_argument("--workload", default="720p", choices=list(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (scales HBM traffic counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is design only "
@@ -71,6 +73,16 @@ def main():
     import torch
 
     import int4_quantized_flashattention_amd as R
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
 
     w = W.WORKLOADS[args.workload]
     t_gen = time.perf_counter()

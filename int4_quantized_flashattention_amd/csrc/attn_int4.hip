@@ -124,8 +124,11 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
       const int o = (tid + i * NT) * 16;
-      if (o < KPK) pre[i] = *reinterpret_cast<const uint4*>(kg + (long long)j * KPK + o);
-      else if (o < PK) pre[i] = *reinterpret_cast<const uint4*>(vg + (long long)j * VPK + (o - KPK));
+      // passes that lie wholly inside the K part or the V part need no per-thread test
+      const bool allK = (i + 1) * NT * 16 <= KPK;
+      const bool allV = i * NT * 16 >= KPK && (i + 1) * NT * 16 <= PK;
+      if (allK || (!allV && o < KPK)) pre[i] = *reinterpret_cast<const uint4*>(kg + (long long)j * KPK + o);
+      else if (allV || o < PK) pre[i] = *reinterpret_cast<const uint4*>(vg + (long long)j * VPK + (o - KPK));
     }
   };
   auto store_block = [&](int stage) {
@@ -134,10 +137,12 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
       const int o = (tid + i * NT) * 16;
-      if (o < KPK) {
+      const bool allK = (i + 1) * NT * 16 <= KPK;
+      const bool allV = i * NT * 16 >= KPK && (i + 1) * NT * 16 <= PK;
+      if (allK || (!allV && o < KPK)) {
         const int r = o / QROW, bo = o - (o / QROW) * QROW;
         store_unpacked(base + r * KROW + 2 * bo, pre[i]);
-      } else if (o < PK) {
+      } else if (allV || o < PK) {
         const int ov = o - KPK, c = ov >> 5, bo = ov & 31;
         store_unpacked(base + KST + c * VROW + 2 * bo, pre[i]);
       }
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
       if (!kRagged) {
         mx = max(s0[0], s1[0]);
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mx = max(mx, max(s0[v], s1[v]));
+        for (int v = 1; v < 16; ++v) mx = max(mx, max(s0[v], s1[v]));   // v_max3_i32
       } else {
         mx = INT_MIN;
 #pragma unroll
@@ -186,15 +191,20 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
           if (k0 + 32 < L) mx = max(mx, s1[v]);
         }
       }
-      mx = max(mx, __shfl_xor(mx, 32));
+      {  // the other 32 keys of this query sit in lane ^ 32
+        const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+        mx = max((int)sw[0], (int)sw[1]);   // the builtin yields unsigned lanes: compare as signed
+      }
       // max over the block of float(acc) * c = float(max acc) * c, as c >= 0
       const float m_new = fmaxf(m_run, fmul_rn((float)mx, cs));
-      if (DUMP || __ballot(m_new > m_run) != 0ull) {
+      const bool flush = DUMP || __ballot(m_new > m_run) != 0ull;
+      if (flush) {
         const float alpha = exp2_hw(fsub_rn(m_run, m_new));
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
+          for (int v = 0; v < 16; ++v)
+          {
             // everything accumulated so far (float and pending int32) is at the old max
             o_acc[ct][v] = alpha * (o_acc[ct][v] + (float)pacc[ct][v]);
             pacc[ct][v] = 0;
