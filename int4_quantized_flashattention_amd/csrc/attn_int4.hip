@@ -66,7 +66,7 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
   constexpr int KST = kBlock * KROW;
   constexpr int STAGE = KST + DV * VROW + 16;   // + the K block scale
   constexpr int NLOAD = (PK + NT * 16 - 1) / (NT * 16);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -83,9 +83,19 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
     h = bh0 - b * kp.H;
     row_base = qb * kBlock;
   } else {
-    b = blockIdx.z;
-    h = blockIdx.y;
-    row_base = blockIdx.x * (32 * NW);
+    // 1D grid. Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+    // contiguous run of (b, h, row tile) so that one head's K/V stream stays in
+    // one XCD's L2 instead of being fetched by all eight.
+    const int ntiles = (L + 32 * NW - 1) / (32 * NW);
+    const int total = kp.B * kp.H * ntiles;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int per = total >> 3, extra = total & 7;   // XCD x gets per + (x < extra) items
+    const int logical = xcd * per + min(xcd, extra) + slot;
+    const int bhl = logical / ntiles;
+    b = bhl / kp.H;
+    h = bhl - b * kp.H;
+    row_base = (logical - bhl * ntiles) * (32 * NW);
   }
   const int bh = b * kp.H + h;
   const int wrow = row_base + 32 * wave;
@@ -117,10 +127,12 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
       while (j < NB && kflag[j] != 0) ++j;   // FP16 tile: the other path takes it
     return j;
   };
+  // Packed codes of a future block wait in registers; store_stage unpacks
+  // them into one of the three LDS stages.
   uint4 pre[NLOAD];
-  float sk_next = 0.f;   // K block scale, carried through LDS with the tile
+  float sk_pre = 0.f;   // K block scale, carried through LDS with the tile
   auto load_block = [&](int j) {
-    if (tid == 0) sk_next = a.k_scale[bh * NB + j];
+    if (tid == 0) sk_pre = a.k_scale[bh * NB + j];
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
       const int o = (tid + i * NT) * 16;
@@ -131,9 +143,9 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
       else if (allV || o < PK) pre[i] = *reinterpret_cast<const uint4*>(vg + (long long)j * VPK + (o - KPK));
     }
   };
-  auto store_block = [&](int stage) {
+  auto store_stage = [&](int stage) {
     uint8_t* base = smem + stage * STAGE;
-    if (tid == 0) *reinterpret_cast<float*>(base + STAGE - 16) = sk_next;
+    if (tid == 0) *reinterpret_cast<float*>(base + STAGE - 16) = sk_pre;
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
       const int o = (tid + i * NT) * 16;
@@ -149,147 +161,205 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
     }
   };
 
+  // O = o_acc * 2^(m_ref - m_run) + pacc: o_acc holds everything folded so far
+  // at a fixed reference max m_ref (per row), pacc the int32 sum since the
+  // last fold at the current running max m_run. A fold is one multiply-add
+  // per value and leaves o_acc unscaled; the reference moves only when
+  // m_run - m_ref exceeds 64 (to keep o_acc far from overflow).
   float m_run = -INFINITY;
-  float l15 = 0.f;                 // row sum of 15 P (lane-partial)
-  v16f o_acc[NCT];                 // float32 O (times 16), flushed from pacc
-  v16i pacc[NCT];                  // int32 O (times 16) since the last flush
+  float m_ref = -INFINITY;
+  float l15 = 0.f;                 // row sum of 15 P (lane-partial), at m_run
+  v16f o_acc[NCT];                 // float32 O (times 16) at m_ref
+  v16i pacc[NCT];                  // int32 O (times 16) at m_run since the last fold
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int v = 0; v < 16; ++v) { o_acc[ct][v] = 0.f; pacc[ct][v] = 0; }
 
-  auto block_step = [&](auto ragged_tag, int stage, int j) {
+  // S^T (times 256) of the block in `stage`, as two 32-key halves
+  v16i s0, s1;
+  auto qk = [&](int stage) {
+    const uint8_t* Ks = smem + stage * STAGE;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { s0[v] = 0; s1[v] = 0; }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const v4i a0 = *reinterpret_cast<const v4i*>(Ks + col * KROW + hh * (DP / 2) + 16 * c);
+      const v4i a1 = *reinterpret_cast<const v4i*>(Ks + (32 + col) * KROW + hh * (DP / 2) + 16 * c);
+      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qop[c], s1, 0, 0, 0);
+    }
+  };
+
+  // Row max, rescale, P codes and P.V of block j (its S^T is in s0/s1, its V in `stage`).
+  auto softmax_pv = [&](auto ragged_tag, int stage, int j) {
     constexpr bool kRagged = decltype(ragged_tag)::value;
-      const uint8_t* Ks = smem + stage * STAGE;
-      const uint8_t* Vs = Ks + KST;
-      // S^T (times 256) for the two 32-key halves of the block
-      v16i s0, s1;
+    const uint8_t* Ks = smem + stage * STAGE;
+    const uint8_t* Vs = Ks + KST;
+    // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly
+    const float sk = *reinterpret_cast<const float*>(Ks + STAGE - 16);
+    const float cs = fmul_rn(fmul_rn(cq, sk), 1.0f / 256.0f);
+    const int key0 = j * kBlock;
+    int mx;
+    if (!kRagged) {
+      // two interleaved max3 chains over the 32 values of this lane
+      int ma = max(s0[0], s1[0]), mb = max(s0[1], s1[1]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) { s0[v] = 0; s1[v] = 0; }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const v4i a0 = *reinterpret_cast<const v4i*>(Ks + col * KROW + hh * (DP / 2) + 16 * c);
-        const v4i a1 = *reinterpret_cast<const v4i*>(Ks + (32 + col) * KROW + hh * (DP / 2) + 16 * c);
-        s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qop[c], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qop[c], s1, 0, 0, 0);
+      for (int v = 2; v < 16; v += 2) {
+        ma = max(max(ma, s0[v]), s1[v]);
+        mb = max(max(mb, s0[v + 1]), s1[v + 1]);
       }
-      // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly
-      const float sk = *reinterpret_cast<const float*>(Ks + STAGE - 16);
-      const float cs = fmul_rn(fmul_rn(cq, sk), 1.0f / 256.0f);
-      const int key0 = j * kBlock;
-      int mx;
-      if (!kRagged) {
-        mx = max(s0[0], s1[0]);
+      mx = max(ma, mb);
+    } else {
+      mx = INT_MIN;
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mx = max(mx, max(s0[v], s1[v]));   // v_max3_i32
-      } else {
-        mx = INT_MIN;
+      for (int v = 0; v < 16; ++v) {
+        const int k0 = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (k0 < L) mx = max(mx, s0[v]);
+        if (k0 + 32 < L) mx = max(mx, s1[v]);
+      }
+    }
+    {  // the other 32 keys of this query sit in lane ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+      mx = max((int)sw[0], (int)sw[1]);   // the builtin yields unsigned lanes: compare as signed
+    }
+    // max over the block of float(acc) * c = float(max acc) * c, as c >= 0
+    const float m_new = fmaxf(m_run, fmul_rn((float)mx, cs));
+    const bool flush = DUMP || __ballot(m_new > m_run) != 0ull;
+    if (flush) {
+      // fold pacc (at m_run) into o_acc (at m_ref); nothing folded yet before the first block
+      const bool first = m_run == -INFINITY;
+      const float g = first ? 0.f : exp2_hw(fsub_rn(m_run, m_ref));
+      m_ref = first ? m_new : m_ref;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o_acc[ct][v] = fmaf((float)pacc[ct][v], g, o_acc[ct][v]);
+      {  // zero the int32 accumulators on the matrix cores (0 x 0 + 0)
+        v4i z4;
+        v16i z16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) z4[v] = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) z16[v] = 0;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(z4, z4, z16, 0, 0, 0);
+      }
+      l15 *= exp2_hw(fsub_rn(m_run, m_new));
+      m_run = m_new;
+      if (__ballot(fsub_rn(m_run, m_ref) > 64.f) != 0ull) {
+        const float f = exp2_hw(fsub_rn(m_ref, m_run));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o_acc[ct][v] *= f;
+        m_ref = m_run;
+      }
+    }
+    // 15 P = 2^(acc c - (m - log2 15)); its rne is pq + 8, packed by v_cvt_pk_u8_f32
+    const float nm15 = -fsub_rn(m_run, log2_15);
+    v4i pop[2];
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int v = 4 * kq + bb;
+          float t = fmaf((float)(s == 0 ? s0[v] : s1[v]), cs, nm15);
+          if (kRagged) {
+            const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
+            if (key >= L) t = -INFINITY;
+          }
+          const float p15 = exp2_hw(t);
+          if (bb & 1) ls1 += p15; else ls0 += p15;
+          word = __builtin_amdgcn_cvt_pk_u8_f32(p15, bb, word);
+          if (DUMP && wrow + col < L) {
+            const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
+            const long long di = ((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key;
+            a.d_acc[di] = (s == 0 ? s0[v] : s1[v]) >> 8;
+            a.d_pq[di] = (int8_t)((int)((word >> (8 * bb)) & 0xFFu) - 8);
+          }
+        }
+        pop[s][kq] = (int)word;
+      }
+    l15 += ls0 + ls1;
+    // O^T += V^T (pq + 8)^T: the zero-point correction rides inside the product
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const v4i vop = *reinterpret_cast<const v4i*>(Vs + (ct * 32 + col) * VROW + 32 * hh + 16 * s);
+        pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pop[s], pacc[ct], 0, 0, 0);
+      }
+    }
+    if (DUMP && wrow + col < L) {
+      const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int k0 = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (k0 < L) mx = max(mx, s0[v]);
-          if (k0 + 32 < L) mx = max(mx, s1[v]);
+          const int ch = ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          a.d_pv[(r * NB + j) * DV + ch] = pacc[ct][v] >> 4;
         }
-      }
-      {  // the other 32 keys of this query sit in lane ^ 32
-        const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
-        mx = max((int)sw[0], (int)sw[1]);   // the builtin yields unsigned lanes: compare as signed
-      }
-      // max over the block of float(acc) * c = float(max acc) * c, as c >= 0
-      const float m_new = fmaxf(m_run, fmul_rn((float)mx, cs));
-      const bool flush = DUMP || __ballot(m_new > m_run) != 0ull;
-      if (flush) {
-        const float alpha = exp2_hw(fsub_rn(m_run, m_new));
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-          {
-            // everything accumulated so far (float and pending int32) is at the old max
-            o_acc[ct][v] = alpha * (o_acc[ct][v] + (float)pacc[ct][v]);
-            pacc[ct][v] = 0;
-          }
-        l15 *= alpha;
-        m_run = m_new;
-      }
-      // 15 P = 2^(acc c - (m - log2 15)); its rne is pq + 8, packed by v_cvt_pk_u8_f32
-      const float nm15 = -fsub_rn(m_run, log2_15);
-      v4i pop[2];
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int v = 4 * kq + bb;
-            float t = fmaf((float)(s == 0 ? s0[v] : s1[v]), cs, nm15);
-            if (kRagged) {
-              const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
-              if (key >= L) t = -INFINITY;
-            }
-            const float p15 = exp2_hw(t);
-            if (bb & 1) ls1 += p15; else ls0 += p15;
-            word = __builtin_amdgcn_cvt_pk_u8_f32(p15, bb, word);
-            if (DUMP && wrow + col < L) {
-              const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
-              const long long di = ((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key;
-              a.d_acc[di] = (s == 0 ? s0[v] : s1[v]) >> 8;
-              a.d_pq[di] = (int8_t)((int)((word >> (8 * bb)) & 0xFFu) - 8);
-            }
-          }
-          pop[s][kq] = (int)word;
-        }
-      l15 += ls0 + ls1;
-      // O^T += V^T (pq + 8)^T: the zero-point correction rides inside the product
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const v4i vop = *reinterpret_cast<const v4i*>(Vs + (ct * 32 + col) * VROW + 32 * hh + 16 * s);
-          pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pop[s], pacc[ct], 0, 0, 0);
-        }
-      }
-      if (DUMP && wrow + col < L) {
-        const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int ch = ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            a.d_pv[(r * NB + j) * DV + ch] = pacc[ct][v] >> 4;
-          }
-        if (hh == 0) a.d_m[r * NB + j] = m_run;
-      }
-      };
+      if (hh == 0) a.d_m[r * NB + j] = m_run;
+    }
+  };
 
-  // Full key blocks in the loop; the ragged last block (keys at or beyond L)
-  // after it, so that the hot loop carries no key mask.
+  // Software pipeline over the key blocks this path takes (ascending), with a
+  // three-stage LDS ring. Entering the iteration for block j: S^T(j) is in
+  // s0/s1, block j+1 is in LDS, the packed codes of block j+2 are in flight.
+  // The iteration runs the softmax of block j (vector ALUs), then issues
+  // P.V(j) and S^T(j+1) on the matrix cores while it unpacks block j+2 into
+  // the stage block j-1 used. One barrier per block. Only the last block can
+  // be ragged; it is taken after the loop.
   const int nfull = L / kBlock;
   int j = next_block(0);
-  if (j < NB) load_block(j);
-  int stage = 0;
-  while (j < nfull) {
-    store_block(stage);
-    __syncthreads();
-    const int jn = next_block(j + 1);
-    if (jn < NB) load_block(jn);
-    if (work) block_step(std::integral_constant<bool, false>(), stage, j);
-    stage ^= 1;
-    j = jn;
-  }
+  int jn = NB, jnn = NB;
   if (j < NB) {
-    store_block(stage);
+    load_block(j);
+    store_stage(0);
+    jn = next_block(j + 1);
+    if (jn < NB) {
+      load_block(jn);
+      store_stage(1);
+      jnn = next_block(jn + 1);
+      if (jnn < NB) load_block(jnn);
+    }
     __syncthreads();
-    if (work) block_step(std::integral_constant<bool, true>(), stage, j);
+    if (work) qk(0);
   }
+  int st = 0;
+  while (j < nfull) {
+    const int st1 = (st == 2) ? 0 : st + 1;
+    const int st2 = (st1 == 2) ? 0 : st1 + 1;
+    if (work) {
+      softmax_pv(std::integral_constant<bool, false>(), st, j);
+      qk(st1);   // stale data when there is no next block: computed, never used
+    }
+    const int j3 = (jnn < NB) ? next_block(jnn + 1) : NB;
+    if (jnn < NB) {
+      store_stage(st2);
+      if (j3 < NB) load_block(j3);
+    }
+    __syncthreads();
+    st = st1;
+    j = jn;
+    jn = jnn;
+    jnn = j3;
+  }
+  if (j < NB && work) softmax_pv(std::integral_constant<bool, true>(), st, j);
 
   if (DUMP || !work) return;
+  {  // O = o_acc 2^(m_ref - m_run) + pacc
+    const float f = (m_run == -INFINITY) ? 0.f : exp2_hw(fsub_rn(m_ref, m_run));
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o_acc[ct][v] += (float)pacc[ct][v];
+      for (int v = 0; v < 16; ++v) o_acc[ct][v] = fmaf(o_acc[ct][v], f, (float)pacc[ct][v]);
+  }
   const float l15t = l15 + __shfl_xor(l15, 32);
   const int row = wrow + col;
   if (row >= L) return;
@@ -342,7 +412,8 @@ static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump
     hipLaunchKernelGGL((int4_attn_kernel<DP, DV, kWaves, true>), dim3(a.n_units), dim3(kWaves * 64), 0, s, kp, a,
                        c0, l15);
   } else {
-    dim3 grid((kp.L + 32 * kWaves - 1) / (32 * kWaves), kp.H, kp.B);
+    const int ntiles = (kp.L + 32 * kWaves - 1) / (32 * kWaves);
+    dim3 grid(ntiles * kp.H * kp.B);
     hipLaunchKernelGGL((int4_attn_kernel<DP, DV, kWaves, false>), grid, dim3(kWaves * 64), 0, s, kp, a, c0, l15);
   }
   return hipGetLastError();
