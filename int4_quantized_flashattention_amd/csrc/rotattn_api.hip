@@ -238,6 +238,7 @@ int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k, 
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
   if (q == nullptr || k == nullptr) return ROTATTN_EINVAL;
   if ((rc = check_qk(out)) != ROTATTN_OK) return rc;
   if (!aligned16(q) || !aligned16(k)) return ROTATTN_EALIGN;
@@ -263,6 +264,7 @@ int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
   if (v == nullptr) return ROTATTN_EINVAL;
   if ((rc = check_v(out)) != ROTATTN_OK) return rc;
   if (!aligned16(v)) return ROTATTN_EALIGN;
@@ -280,6 +282,7 @@ int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, co
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
   if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
   if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
   if ((rc = check_attention_args(p, qk, v, head_fallback, out)) != ROTATTN_OK) return rc;
@@ -295,6 +298,7 @@ int rotattn_forward(const rotattn_problem* p, const rotattn_qk_buffers* qk, cons
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
   if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
   if (v == nullptr) return ROTATTN_EINVAL;
   if (!aligned16(v)) return ROTATTN_EALIGN;
@@ -315,6 +319,7 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return ROTATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ROTATTN_EALIGN;
   const Layout L = layout(p, d, ROTATTN_CALL_FP16_FORWARD);
@@ -342,6 +347,7 @@ int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, c
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
   if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
   if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
   if (n_units < 0 || (n_units > 0 && (!units || !acc_qk || !p_codes || !acc_pv || !m_hist))) return ROTATTN_EINVAL;

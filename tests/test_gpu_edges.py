@@ -1,0 +1,133 @@
+"""Edge cases of the HIP path against the oracle: tiny and ragged lengths, text-only
+sequences, strided layouts with B > 1, degenerate inputs, the empty problem and
+the dump hook's bounds handling."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import core as O
+from tests import gpu_common as G
+
+torch = G.torch
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(w, x, layout="bhld", tau=None, head_mask=None):
+    """quantize_qk + forward through the C ABI; check codes and outputs against the oracle for every head."""
+    B, H, L, D = w.B, w.H, w.L, w.D
+    if layout == "blhd":   # [B, L, H, D] storage viewed as [B, H, L, D]
+        def put(a):
+            return torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).cuda().permute(0, 2, 1, 3)
+        strides = (L * H * D, D, H * D)
+        out = torch.empty((B, L, H, D), dtype=torch.float16, device="cuda").permute(0, 2, 1, 3)
+    else:
+        def put(a):
+            return G.dev(a)
+        strides = None
+        out = torch.empty((B, H, L, D), dtype=torch.float16, device="cuda")
+    q, k, v = put(x["q"]), put(x["k"]), put(x["v"])
+    p = G.R.problem_from_workload(w, strides=strides, tau=tau)
+    need_rope = head_mask is not None or (tau is not None and np.isfinite(tau))
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=need_rope)
+    m = G.dev(head_mask) if head_mask is not None else None
+    G.R.rotattn_forward(p, qk, v, head_fallback=m, out=out)
+    got = G.host(out).astype(np.float64)
+    qc = G.unpack_qk_codes(G.host(qk.q_codes))
+    for b in range(B):
+        for h in range(H):
+            masked = head_mask is not None and bool(head_mask[b * H + h])
+            o = G.oracle_head(w, x, b, h, tau=tau, head_masked=masked,
+                              q_flags=G.host(qk.q_flag)[b, h].astype(bool),
+                              k_flags=G.host(qk.k_flag)[b, h].astype(bool))
+            assert np.array_equal(qc[b, h], o["q"]["codes"]), (b, h)
+            tol = G.ATOL + G.RTOL * np.abs(o["out"])
+            if masked:
+                _, bound = G.fp16_weight_bound(o["q"]["rope16"], o["k"]["rope16"], x["v"][b, h], L, D, np.arange(L))
+                tol = tol + bound
+            err = np.abs(got[b, h] - o["out"])
+            assert (err <= tol).all(), (b, h, float(err.max()))
+    return got
+
+
+@pytest.mark.parametrize("grid,prefix", [((1, 1, 1), 0), ((1, 8, 8), 0), ((1, 5, 13), 0), ((0, 0, 0), 100),
+                                         ((1, 1, 3), 61)])
+def test_lengths(grid, prefix):
+    """L = 1, one full block, one block plus one token, a text-only sequence, a block boundary inside the prefix."""
+    G.require_gpu()
+    w = W.WORKLOADS["tiny"].replace(grid=grid, prefix=prefix)
+    _run_and_check(w, W.full_inputs(w))
+
+
+def test_strided_batch_layout():
+    """B = 2 with tokens-major [B, L, H, D] storage (non-dense strides), D = 64, text prefix."""
+    G.require_gpu()
+    w = W.WORKLOADS["smalld"].replace(B=2, H=3, grid=(2, 3, 17), prefix=9)
+    _run_and_check(w, W.full_inputs(w), layout="blhd")
+
+
+def test_degenerate_inputs():
+    """Q = 0 (every P = 1), an all-zero K block (scale 0), negative scores everywhere (K = -Q)."""
+    G.require_gpu()
+    w = W.WORKLOADS["tiny"].replace(H=3, grid=(1, 10, 20))
+    x = W.full_inputs(w)
+    x["q"][:, 0] = 0
+    x["k"][:, 1, 64:128] = 0
+    x["k"][:, 2] = -x["q"][:, 2]
+    _run_and_check(w, x)
+
+
+def test_mask_and_block_rule_small():
+    """Head mask and the 5% block rule together at a small size, against the oracle's routing."""
+    G.require_gpu()
+    w = W.WORKLOADS["mixed"].replace(H=4, grid=(3, 7, 9))
+    x = W.full_inputs(w)
+    # plant a high-norm token so that one K block is flagged for sure
+    x["k"][0, 1, 70] *= np.float16(12)
+    mask = np.array([0, 0, 1, 0], dtype=np.uint8)
+    _run_and_check(w, x, tau=0.05, head_mask=mask)
+
+
+def test_empty_problem():
+    """L = 0: every call returns success and touches nothing."""
+    G.require_gpu()
+    p = G.R.make_problem(1, 2, 0, 128, (0, 0, 0), 0, (44, 42, 42))
+    z = torch.zeros(16, dtype=torch.float16, device="cuda")
+    qk = G.R.binding.alloc_qk(p, "cuda", False)
+    G.R.rotattn_quantize_qk(p, z, z, out=qk)
+    G.R.rotattn_forward(p, qk, z, out=z)
+    torch.cuda.synchronize()
+
+
+def test_dump_ignores_out_of_range_units():
+    """Units outside [0, B*H*NB) are skipped by the kernel: their dump rows stay as the caller filled them."""
+    G.require_gpu()
+    w = W.WORKLOADS["tiny"]
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    qk = G.R.rotattn_quantize_qk(p, G.dev(x["q"]), G.dev(x["k"]))
+    vq = G.R.rotattn_quantize_v(p, G.dev(x["v"]))
+    d = G.R.rotattn_debug_dump(p, qk, vq, G.dev(np.array([-1, 10**6, 1], dtype=np.int32)))
+    acc = G.host(d["acc"])
+    assert not acc[0].any() and not acc[1].any() and acc[2].any()
+
+
+def test_fp16_forward_strided():
+    """The whole-call FP16 path with [B, L, H, D] storage."""
+    G.require_gpu()
+    w = W.WORKLOADS["tiny"].replace(B=2, H=2, grid=(1, 6, 25), prefix=5)
+    x = W.full_inputs(w)
+    B, H, L, D = w.B, w.H, w.L, w.D
+
+    def put(a):
+        return torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).cuda().permute(0, 2, 1, 3)
+    out = torch.empty((B, L, H, D), dtype=torch.float16, device="cuda").permute(0, 2, 1, 3)
+    p = G.R.problem_from_workload(w, strides=(L * H * D, D, H * D))
+    G.R.rotattn_fp16_forward(p, put(x["q"]), put(x["k"]), put(x["v"]), out=out)
+    got = G.host(out).astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            qr = O.apply_rope(x["q"][b, h].astype(np.float32), w.prefix, w.grid, w.split, w.base).astype(np.float16)
+            kr = O.apply_rope(x["k"][b, h].astype(np.float32), w.prefix, w.grid, w.split, w.base).astype(np.float16)
+            pp, bound = G.fp16_weight_bound(qr, kr, x["v"][b, h], L, D, np.arange(L))
+            ref = pp["O"] / pp["l"][:, None]
+            assert (np.abs(got[b, h] - ref) <= G.ATOL + G.RTOL * np.abs(ref) + bound).all()
