@@ -31,10 +31,35 @@ import workloads as W  # noqa: E402
 METRIC = "attention TOPS (4·B·H·L²·D/s) and % of INT8 MFMA peak, 75600-token 40-head"
 INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 matrix-core peak, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("int4_quantized_flashattention_amd/csrc/attn_int4.hip", "int4_quantized_flashattention_amd/csrc/common.h")
 
 
-def cpu_baseline(w: W.Workload, x, rows_sample: int = 1024):
-    """Oracle (numpy, 1 BLAS thread) on head 0: its prologue plus the flash loop for `rows_sample` query rows."""
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the INT4 attention kernel, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload (calibrated against a plain copy), or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"int4_attn_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            vals[k] = v
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(w: W.Workload, x, seconds: float = 12.0, chunk: int = 512):
+    """Oracle (numpy, 1 BLAS thread) on head 0: its Q/K/V prologue, then the INT4 flash loop over all keys
+    for consecutive chunks of `chunk` query rows until `seconds` of CPU time have passed (at least one chunk).
+    Only the flash-loop rows are credited with ops; the prologue time is included in the denominator."""
     from threadpoolctl import threadpool_limits
 
     from oracle import core as O
@@ -44,14 +69,19 @@ def cpu_baseline(w: W.Workload, x, rows_sample: int = 1024):
         qp = O.qk_prologue(q, w.prefix, w.grid, w.split, w.base, w.rotation)
         kp = O.qk_prologue(k, w.prefix, w.grid, w.split, w.base, w.rotation)
         vc, sv, cs = O.quantize_v(v)
-        rows = np.arange(min(rows_sample, w.L))
-        O.int4_flash_rows(qp["codes"], qp["scale"], kp["codes"], kp["scale"], vc, sv, cs, w.L, w.D, rows)
+        t_pro = time.perf_counter() - t0
+        done = 0
+        while done < w.L and (done == 0 or time.perf_counter() - t0 < seconds):
+            rows = np.arange(done, min(done + chunk, w.L))
+            O.int4_flash_rows(qp["codes"], qp["scale"], kp["codes"], kp["scale"], vc, sv, cs, w.L, w.D, rows)
+            done += rows.size
         dt = time.perf_counter() - t0
-    ops = 4.0 * rows.size * w.L * w.D
+    ops = 4.0 * done * w.L * w.D
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": f"head 0 of {w.name}: Q/K/V prologue of all {w.L} tokens + INT4 flash loop for "
-                      f"{rows.size} query rows over all keys ({dt:.1f} s; ops credited for the rows only)",
-            "seconds": dt}
+            "sample": f"head 0 of {w.name}: Q/K/V prologue of all {w.L} tokens ({t_pro:.1f} s) + INT4 flash loop "
+                      f"for query rows 0..{done - 1} over all {w.L} keys; {dt:.1f} s in total on 1 thread, "
+                      f"ops credited for those {done} rows only",
+            "seconds": round(dt, 2)}
 
 
 def main():
@@ -61,7 +91,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p", choices=list(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time bound of the oracle baseline sample (whole 512-row chunks)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (scales HBM traffic counters) and exit")
     args = ap.parse_args()
@@ -147,7 +178,7 @@ def main():
                                f"prefix={w.prefix} rotation={'group64' if w.rotation else 'full'}",
                    "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.D, "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(w.name), "traffic_unit": "HBM bytes per launch",
                      "kernel": "int4_attn_kernel (rotattn_attention)", "avg_ms": round(att_ms, 4)},
         "breakdown_ms": {"quantize_qk": round(float(t_qk.mean()), 4), "quantize_v": round(float(t_v.mean()), 4),
                          "attention": round(att_ms, 4),
@@ -155,7 +186,7 @@ def main():
         "wall_s_timed": round(wall, 3), "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(rec))
 
 
