@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ROTATTN_VERSION 1
+#define ROTATTN_VERSION 2
 
 /* error codes */
 #define ROTATTN_OK            0
@@ -165,7 +165,9 @@ int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_
  * non-NULL or block_err_tau is finite, qk->q_rope and qk->k_rope and v are
  * required (the FP16 path reads them); otherwise they may be NULL.
  * out: device fp16 with the problem's strides (may not alias inputs).
- * Workspace: ROTATTN_CALL_ATTENTION bytes.
+ * Workspace: ROTATTN_CALL_ATTENTION bytes: the int8 K/V block images the
+ * INT4 kernel copies into LDS (about 2.5x the packed K + V codes), plus the
+ * partial results of mixed rows when block_err_tau is finite.
  */
 int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                       const void* v, const uint8_t* head_fallback, void* out,
@@ -199,11 +201,12 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
  *                                      (= pq . v + 8 * colsum)
  *   m_hist  float [n_units][64][NB]   running max (log2 domain) after each block
  * Rows at or beyond L are not written. head_fallback as in rotattn_attention.
+ * Workspace: ROTATTN_CALL_DEBUG_DUMP bytes (the K/V block images).
  */
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                        const uint8_t* head_fallback, const int32_t* units, int32_t n_units,
                        int32_t* acc_qk, int8_t* p_codes, int32_t* acc_pv, float* m_hist,
-                       rotattn_stream_t stream);
+                       void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
 
 #ifdef __cplusplus
 }

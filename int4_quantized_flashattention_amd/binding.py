@@ -80,7 +80,7 @@ def load_library(path: str = LIB_PATH):
     lib.rotattn_forward.argtypes = [P(Problem), P(QKBuffers), vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_fp16_forward.argtypes = [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_debug_dump.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, C.c_int32,
-                                       vp, vp, vp, vp, vp]
+                                       vp, vp, vp, vp, vp, C.c_size_t, vp]
     for name in EXPORTS:
         if name not in ("rotattn_strerror",):
             getattr(lib, name).restype = C.c_int
@@ -289,7 +289,7 @@ def rotattn_fp16_forward(p: Problem, q, k, v, out=None, ws=None, stream=None):
     return out
 
 
-def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback=None, stream=None):
+def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback=None, ws=None, stream=None):
     """Intermediate integers of the INT4 kernel for 64-row query blocks `units` ((b*H+h)*NB + block)."""
     torch = _torch()
     dev = qk.q_codes.device
@@ -300,10 +300,11 @@ def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback
     pq = torch.zeros((n, 64, s.Lp), dtype=torch.int8, device=dev)
     pv = torch.zeros((n, 64, s.NB, p.D), dtype=torch.int32, device=dev)
     m = torch.full((n, 64, s.NB), float("nan"), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(p, CALL_DEBUG_DUMP, dev, ws)
     qs, vs = qk.struct(), vq.struct()
     _check(load_library().rotattn_debug_dump(C.byref(p), C.byref(qs), C.byref(vs), _ptr(head_fallback),
                                              _ptr(units), n, _ptr(acc), _ptr(pq), _ptr(pv), _ptr(m),
-                                             _stream(stream)), "rotattn_debug_dump")
+                                             _ptr(ws), nws, _stream(stream)), "rotattn_debug_dump")
     return {"acc": acc, "pq": pq, "accpv": pv, "m": m}
 
 

@@ -44,6 +44,47 @@ __device__ __forceinline__ void store_unpacked(uint8_t* dst, uint4 p) {
   reinterpret_cast<uint4*>(dst)[1] = b;
 }
 
+// Expands one (b, h, key block) into the LDS image the attention kernel copies:
+// the packed K codes of its 64 keys and the operand-order V codes of its
+// channels become int8 operands (each code times 16) at their padded LDS
+// offsets, and the K block scale goes into the slot after them. Pad bytes are
+// never read and are left as they are.
+template <int DP, int DV>
+__global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_t* __restrict__ k_codes,
+                                                       const float* __restrict__ k_scale,
+                                                       const uint8_t* __restrict__ v_codes, uint8_t* image) {
+  constexpr int QROW = DP / 2, KPK = kBlock * DP / 2, VPK = DV * 32;
+  constexpr int KROW = kv_krow(DP), VROW = kv_vrow(), KST = kv_kst(DP), IMG = kv_image_bytes(DP, DV);
+  const long long u = blockIdx.x;   // (b * H + h) * NB + block
+  const long long bh = u / kp.NB;
+  const int j = (int)(u - bh * kp.NB);
+  uint8_t* dst = image + u * IMG;
+  const uint8_t* kg = k_codes + (bh * kp.Lp + (long long)j * kBlock) * QROW;
+  const uint8_t* vg = v_codes + u * VPK;
+  for (int o = threadIdx.x * 16; o < KPK; o += 256 * 16)
+    store_unpacked(dst + (o / QROW) * KROW + 2 * (o % QROW), *reinterpret_cast<const uint4*>(kg + o));
+  for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16)
+    store_unpacked(dst + KST + (o >> 5) * VROW + 2 * (o & 31), *reinterpret_cast<const uint4*>(vg + o));
+  if (threadIdx.x == 0) *reinterpret_cast<float4*>(dst + kv_scale_off(DP, DV)) = make_float4(k_scale[u], 0.f, 0.f, 0.f);
+}
+
+// s_waitcnt that waits until at most N vector-memory operations of this wave
+// are outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier without a memory fence: LDS stages are filled by
+// direct-to-LDS loads whose completion the caller has already waited for.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
 // 64: the packed K and V codes (prefetched into registers during the previous
 // block) are unpacked once into one of two LDS stages, one barrier, then every
@@ -51,22 +92,34 @@ __device__ __forceinline__ void store_unpacked(uint8_t* dst, uint4 p) {
 // matrix cores. O is accumulated in int32 by the matrix cores and folded into
 // the float32 accumulator only when some row max of the wave grows (the
 // rescale factor is exactly 1 otherwise).
-template <int DP, int DV, int NW, bool DUMP>
-__global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
+template <int DP, int DV, int NW, int NST, int OCC, bool DUMP>
+__global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
   constexpr int NC = DP / 32;              // 32-deep slices of the rotated head dim
   constexpr int NCT = DV / 32;             // 32-channel output tiles
   constexpr int QROW = DP / 2;             // packed code bytes per token
   constexpr int HALF = DP / 4;             // packed code bytes of one lane half
-  constexpr int KPK = kBlock * DP / 2;     // packed K bytes per key block
-  constexpr int VPK = DV * 32;             // packed V bytes per key block
-  constexpr int PK = KPK + VPK;
-  constexpr int KROW = DP + 16;            // unpacked K row in LDS (padded)
-  constexpr int VROW = 64 + 16;            // unpacked V channel row in LDS (padded)
-  constexpr int KST = kBlock * KROW;
-  constexpr int STAGE = KST + DV * VROW + 16;   // + the K block scale
-  constexpr int NLOAD = (PK + NT * 16 - 1) / (NT * 16);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * STAGE];
+  constexpr int KROW = kv_krow(DP);        // int8 K row in LDS (padded)
+  constexpr int VROW = kv_vrow();          // int8 V channel row in LDS (padded)
+  constexpr int KST = kv_kst(DP);
+  constexpr int IMG = kv_image_bytes(DP, DV);   // one LDS stage = one block's image
+  constexpr int NDMA = IMG / (NT * 16);    // 16-byte direct-to-LDS loads per thread per block
+  static_assert(IMG % (NT * 16) == 0, "a stage must split evenly over the workgroup");
+  static_assert(NST == 3 || NST == 4, "three or four LDS stages");
+  // One LDS array per stage, always indexed by a compile-time stage number:
+  // the compiler then knows that reads of one stage cannot alias the
+  // direct-to-LDS copies into another and does not wait for those copies.
+  __shared__ __attribute__((aligned(16))) uint8_t stg0[IMG];
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[IMG];
+  __shared__ __attribute__((aligned(16))) uint8_t stg2[IMG];
+  __shared__ __attribute__((aligned(16))) uint8_t stg3[NST == 4 ? IMG : 16];
+  auto stage = [&](auto s_tag) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int S = decltype(s_tag)::value;
+    if constexpr (S == 0) return stg0;
+    else if constexpr (S == 1) return stg1;
+    else if constexpr (S == 2) return stg2;
+    else return stg3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -119,46 +172,27 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
     cq = fmul_rn(a.q_scale[bh * NB + qblk], c0);
   }
 
-  const uint8_t* kg = a.k_codes + (long long)bh * Lp * QROW;
-  const uint8_t* vg = a.v_codes + (long long)bh * NB * VPK;
   const uint8_t* kflag = a.route ? a.k_flag + (long long)bh * NB : nullptr;
-  auto next_block = [&](int j) {
+  // the next key block at or after j that this path takes (NB if none); the
+  // result is wave-uniform, which keeps the loop control in scalar registers
+  auto next_block = [&](int j) __attribute__((always_inline)) {
     if (kflag != nullptr)
       while (j < NB && kflag[j] != 0) ++j;   // FP16 tile: the other path takes it
-    return j;
+    return __builtin_amdgcn_readfirstlane(j);
   };
-  // Packed codes of a future block wait in registers; store_stage unpacks
-  // them into one of the three LDS stages.
-  uint4 pre[NLOAD];
-  float sk_pre = 0.f;   // K block scale, carried through LDS with the tile
-  auto load_block = [&](int j) {
-    if (tid == 0) sk_pre = a.k_scale[bh * NB + j];
+  // Block j's image goes to LDS stage `stage` with NDMA direct-to-LDS loads per
+  // thread: thread t copies bytes 16t + 4096i of the image, and the hardware
+  // writes lane l's 16 bytes at the wave's LDS base + 16 l.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* img = a.kv_image + (long long)bh * NB * IMG;   // wave-uniform
+  const int toff = tid * 16;                                     // this thread's piece of every round
+  auto dma_block = [&](int j, uint8_t* stage_base) __attribute__((always_inline)) {
+    const uint8_t* src = img + (long long)j * IMG;
+    uint8_t* dst = stage_base + wave_u * 1024;
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) {
-      const int o = (tid + i * NT) * 16;
-      // passes that lie wholly inside the K part or the V part need no per-thread test
-      const bool allK = (i + 1) * NT * 16 <= KPK;
-      const bool allV = i * NT * 16 >= KPK && (i + 1) * NT * 16 <= PK;
-      if (allK || (!allV && o < KPK)) pre[i] = *reinterpret_cast<const uint4*>(kg + (long long)j * KPK + o);
-      else if (allV || o < PK) pre[i] = *reinterpret_cast<const uint4*>(vg + (long long)j * VPK + (o - KPK));
-    }
-  };
-  auto store_stage = [&](int stage) {
-    uint8_t* base = smem + stage * STAGE;
-    if (tid == 0) *reinterpret_cast<float*>(base + STAGE - 16) = sk_pre;
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) {
-      const int o = (tid + i * NT) * 16;
-      const bool allK = (i + 1) * NT * 16 <= KPK;
-      const bool allV = i * NT * 16 >= KPK && (i + 1) * NT * 16 <= PK;
-      if (allK || (!allV && o < KPK)) {
-        const int r = o / QROW, bo = o - (o / QROW) * QROW;
-        store_unpacked(base + r * KROW + 2 * bo, pre[i]);
-      } else if (allV || o < PK) {
-        const int ov = o - KPK, c = ov >> 5, bo = ov & 31;
-        store_unpacked(base + KST + c * VROW + 2 * bo, pre[i]);
-      }
-    }
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_global_load_lds(src + (toff + i * NT * 16),
+                                       (__attribute__((address_space(3))) void*)(dst + i * NT * 16), 16, 0, 0);
   };
 
   // O = o_acc * 2^(m_ref - m_run) + pacc: o_acc holds everything folded so far
@@ -178,8 +212,7 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
 
   // S^T (times 256) of the block in `stage`, as two 32-key halves
   v16i s0, s1;
-  auto qk = [&](int stage) {
-    const uint8_t* Ks = smem + stage * STAGE;
+  auto qk = [&](const uint8_t* Ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) { s0[v] = 0; s1[v] = 0; }
 #pragma unroll
@@ -192,12 +225,11 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
   };
 
   // Row max, rescale, P codes and P.V of block j (its S^T is in s0/s1, its V in `stage`).
-  auto softmax_pv = [&](auto ragged_tag, int stage, int j) {
+  auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, int j) __attribute__((always_inline)) {
     constexpr bool kRagged = decltype(ragged_tag)::value;
-    const uint8_t* Ks = smem + stage * STAGE;
     const uint8_t* Vs = Ks + KST;
     // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly
-    const float sk = *reinterpret_cast<const float*>(Ks + STAGE - 16);
+    const float sk = *reinterpret_cast<const float*>(Ks + kv_scale_off(DP, DV));
     const float cs = fmul_rn(fmul_rn(cq, sk), 1.0f / 256.0f);
     const int key0 = j * kBlock;
     int mx;
@@ -308,49 +340,69 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
     }
   };
 
-  // Software pipeline over the key blocks this path takes (ascending), with a
-  // three-stage LDS ring. Entering the iteration for block j: S^T(j) is in
-  // s0/s1, block j+1 is in LDS, the packed codes of block j+2 are in flight.
-  // The iteration runs the softmax of block j (vector ALUs), then issues
-  // P.V(j) and S^T(j+1) on the matrix cores while it unpacks block j+2 into
-  // the stage block j-1 used. One barrier per block. Only the last block can
-  // be ragged; it is taken after the loop.
+  // Software pipeline over the key blocks this path takes (ascending), with an
+  // NST-stage LDS ring filled by direct-to-LDS loads. q[0..NST-1] are the next
+  // blocks to process. Entering the iteration for block q[0]: S^T(q[0]) is in
+  // s0/s1, q[1] is in LDS, q[2..NST-2] are in flight. The iteration first
+  // starts the copy of q[NST-1] into the stage q[0]'s predecessor used, runs
+  // the softmax of q[0] (vector ALUs), issues P.V(q[0]) and S^T(q[1]) on the
+  // matrix cores, waits for q[2]'s copy and ends with one barrier. Only the
+  // last block can be ragged; it is taken after the loop.
   const int nfull = L / kBlock;
-  int j = next_block(0);
-  int jn = NB, jnn = NB;
-  if (j < NB) {
-    load_block(j);
-    store_stage(0);
-    jn = next_block(j + 1);
-    if (jn < NB) {
-      load_block(jn);
-      store_stage(1);
-      jnn = next_block(jn + 1);
-      if (jnn < NB) load_block(jnn);
-    }
-    __syncthreads();
-    if (work) qk(0);
-  }
-  int st = 0;
-  while (j < nfull) {
-    const int st1 = (st == 2) ? 0 : st + 1;
-    const int st2 = (st1 == 2) ? 0 : st1 + 1;
+  int q[NST];
+  q[0] = next_block(0);
+#pragma unroll
+  for (int i = 1; i < NST; ++i) q[i] = (q[i - 1] < NB) ? next_block(q[i - 1] + 1) : NB;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (q[0] < NB) dma_block(q[0], stage(I0()));
+  if (q[1] < NB) dma_block(q[1], stage(I1()));
+  if (NST == 4 && q[2] < NB) dma_block(q[2], stage(I2()));
+  // q[0] and q[1] must have landed; with four stages q[2] may stay in flight
+  if (DUMP || NST == 3 || q[2] >= NB) wait_vmcnt<0>();
+  else wait_vmcnt<NDMA>();
+  stage_barrier();
+  if (q[0] < NB && work) qk(stage(I0()));
+  // one iteration with q[0] in stage S
+  auto iter = [&](auto s_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_tag)::value;
+    using S1 = std::integral_constant<int, (S + 1) % NST>;
+    using SL = std::integral_constant<int, (S + NST - 1) % NST>;   // the previous block's stage
+    const bool issued = q[NST - 1] < NB;
+    if (issued) dma_block(q[NST - 1], stage(SL()));
     if (work) {
-      softmax_pv(std::integral_constant<bool, false>(), st, j);
-      qk(st1);   // stale data when there is no next block: computed, never used
+      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), q[0]);
+      qk(stage(S1()));   // stale data when there is no next block: computed, never used
     }
-    const int j3 = (jnn < NB) ? next_block(jnn + 1) : NB;
-    if (jnn < NB) {
-      store_stage(st2);
-      if (j3 < NB) load_block(j3);
+    // q[2] must have landed before the next iteration reads it
+    if (DUMP || NST == 3 || !issued) wait_vmcnt<0>();
+    else wait_vmcnt<NDMA>();
+    stage_barrier();
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i) q[i] = q[i + 1];
+    q[NST - 1] = (q[NST - 2] < NB) ? next_block(q[NST - 2] + 1) : NB;
+  };
+  int st = 0;   // stage of q[0] when the loop ends
+  for (;;) {
+    if (q[0] >= nfull) { st = 0; break; }
+    iter(I0());
+    if (q[0] >= nfull) { st = 1; break; }
+    iter(I1());
+    if (q[0] >= nfull) { st = 2; break; }
+    iter(I2());
+    if constexpr (NST == 4) {
+      if (q[0] >= nfull) { st = 3; break; }
+      iter(I3());
     }
-    __syncthreads();
-    st = st1;
-    j = jn;
-    jn = jnn;
-    jnn = j3;
   }
-  if (j < NB && work) softmax_pv(std::integral_constant<bool, true>(), st, j);
+  const int j = q[0];
+  if (j < NB && work) {
+    wait_vmcnt<0>();
+    const uint8_t* Ks = st == 0 ? stage(I0()) : st == 1 ? stage(I1()) : st == 2 ? stage(I2()) : stage(I3());
+    softmax_pv(std::integral_constant<bool, true>(), Ks, j);
+  }
 
   if (DUMP || !work) return;
   {  // O = o_acc 2^(m_ref - m_run) + pacc
@@ -399,24 +451,48 @@ __global__ __launch_bounds__(NW * 64, 2) void int4_attn_kernel(KProblem kp, Attn
   }
 }
 
-// waves per workgroup (32 query rows each): four, so that two independent
-// workgroups share a CU and one's softmax overlaps the other's matrix work
-template <int DP>
-constexpr int waves_for() { return 4; }
+// Launch shape per rotated head dim: waves per workgroup (32 query rows each),
+// LDS stages and workgroups per CU. Four waves, so that independent
+// workgroups share a CU and one's softmax overlaps another's matrix work; four
+// stages where two workgroups' rings still fit in the 160 KB of LDS.
+template <int DP, int DV>
+struct Shape {
+  static constexpr int kWaves = 4;
+  // two workgroups' rings plus a few hundred bytes of other LDS must fit in 160 KB
+  static constexpr int kStages = (2 * 4 * kv_image_bytes(DP, DV) + 1024 <= 160 * 1024) ? 4 : 3;
+  static constexpr int kOcc = 2;
+};
 
 template <int DP, int DV>
 static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump, float c0, float l15,
                                 hipStream_t s) {
-  constexpr int kWaves = waves_for<DP>();
+  using S = Shape<DP, DV>;
+  constexpr int W = S::kWaves, NS = S::kStages, OC = S::kOcc;
   if (dump) {
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, kWaves, true>), dim3(a.n_units), dim3(kWaves * 64), 0, s, kp, a,
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true>), dim3(a.n_units), dim3(W * 64), 0, s, kp, a,
                        c0, l15);
   } else {
-    const int ntiles = (kp.L + 32 * kWaves - 1) / (32 * kWaves);
+    const int ntiles = (kp.L + 32 * W - 1) / (32 * W);
     dim3 grid(ntiles * kp.H * kp.B);
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, kWaves, false>), grid, dim3(kWaves * 64), 0, s, kp, a, c0, l15);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false>), grid, dim3(W * 64), 0, s, kp, a, c0, l15);
   }
   return hipGetLastError();
+}
+
+template <int DP, int DV>
+static hipError_t launch_kv_image_t(const KProblem& kp, const AttnArgs& a, uint8_t* image, hipStream_t s) {
+  const long long units = (long long)kp.B * kp.H * kp.NB;
+  hipLaunchKernelGGL((kv_image_kernel<DP, DV>), dim3((unsigned)units), dim3(256), 0, s, kp, a.k_codes, a.k_scale,
+                     a.v_codes, image);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_image(const KProblem& kp, const AttnArgs& a, uint8_t* image, hipStream_t s) {
+  if (kp.Dp == 128 && kp.D == 128) return launch_kv_image_t<128, 128>(kp, a, image, s);
+  if (kp.Dp == 192 && kp.D == 128) return launch_kv_image_t<192, 128>(kp, a, image, s);
+  if (kp.Dp == 64 && kp.D == 64) return launch_kv_image_t<64, 64>(kp, a, image, s);
+  if (kp.Dp == 192 && kp.D == 64) return launch_kv_image_t<192, 64>(kp, a, image, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_int4_attention(const KProblem& kp, const AttnArgs& a, bool dump, hipStream_t s) {

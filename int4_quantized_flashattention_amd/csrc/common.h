@@ -48,6 +48,20 @@ __device__ __forceinline__ v4i unpack16(uint2 p) {
   return r;
 }
 
+// LDS stage of one 64-key block in the INT4 attention kernel, and the byte image
+// of it in HBM that the kernel copies with direct-to-LDS loads: 64 K rows of DP
+// int8 operand bytes padded to DP + 16 (against bank conflicts), then DV V
+// channel rows of 64 int8 operand bytes padded to 80, then the K block scale in
+// a 16-byte slot; the whole rounded up to a multiple of 4096 bytes so that every
+// thread of a 256-thread workgroup copies the same number of 16-byte pieces.
+__host__ __device__ constexpr int kv_krow(int DP) { return DP + 16; }
+__host__ __device__ constexpr int kv_vrow() { return 64 + 16; }
+__host__ __device__ constexpr int kv_kst(int DP) { return kBlock * kv_krow(DP); }
+__host__ __device__ constexpr int kv_scale_off(int DP, int DV) { return kv_kst(DP) + DV * kv_vrow(); }
+__host__ __device__ constexpr int kv_image_bytes(int DP, int DV) {
+  return (kv_scale_off(DP, DV) + 16 + 4095) / 4096 * 4096;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
@@ -78,6 +92,7 @@ struct AttnArgs {
   const uint32_t* head_kflag;
   const uint8_t* head_mask;     // [B*H] or null
   const uint8_t* v_codes; const float* v_scale;
+  const uint8_t* kv_image;      // [B*H][NB] LDS images of the K/V blocks (kv_image_bytes each)
   const __half* q_rope; const __half* k_rope; const __half* v;   // FP16 path inputs
   __half* out;
   float* part_o; float* part_m; float* part_l;   // INT4 partials of mixed rows [B][H][Lp][D], [B][H][Lp]
@@ -92,6 +107,7 @@ hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half*
                               const QKOut& o, hipStream_t s);
 hipError_t launch_rope_copy(const KProblem& kp, const __half* x, const float* tab, __half* dst, hipStream_t s);
 hipError_t launch_vquant(const KProblem& kp, const __half* v, uint32_t* absmax_bits, const VOut& o, hipStream_t s);
+hipError_t launch_kv_image(const KProblem& kp, const AttnArgs& a, uint8_t* image, hipStream_t s);
 hipError_t launch_int4_attention(const KProblem& kp, const AttnArgs& a, bool dump, hipStream_t s);
 hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, bool whole_call, hipStream_t s);
 }  // namespace rotattn

@@ -75,7 +75,7 @@ int derive(const rotattn_problem* p, Derived* d) {
 
 // Workspace carve-up of every call. Offsets are 256-byte aligned.
 struct Layout {
-  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0;
+  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0, img = 0;
   size_t total = 0;
 };
 
@@ -94,6 +94,7 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
   const size_t po_b = (size_t)BH * d.Lp * p->D * sizeof(float);
   const size_t pm_b = (size_t)BH * d.Lp * sizeof(float);
   const size_t rope_b = (size_t)BH * p->L * p->D * 2;
+  const size_t img_b = (size_t)BH * d.NB * kv_image_bytes((int)d.Dp, p->D);
   switch (call) {
     case ROTATTN_CALL_QUANTIZE_QK:
       L.tab = take(tab_bytes);
@@ -102,17 +103,21 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
       L.absmax = take(absmax_b);
       break;
     case ROTATTN_CALL_ATTENTION:
+      L.img = take(img_b);
       if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
       break;
     case ROTATTN_CALL_FORWARD:
       L.vcodes = take(vcodes_b); L.vscale = take(vscale_b); L.vcolsum = take(vcolsum_b);
       L.absmax = take(absmax_b);
+      L.img = take(img_b);
       if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
       break;
     case ROTATTN_CALL_FP16_FORWARD:
       L.tab = take(tab_bytes); L.qr = take(rope_b); L.kr = take(rope_b);
       break;
     case ROTATTN_CALL_DEBUG_DUMP:
+      L.img = take(img_b);
+      break;
     default:
       break;
   }
@@ -168,7 +173,11 @@ int attention_impl(const rotattn_problem* p, const Derived& d, const rotattn_qk_
   a.out = static_cast<__half*>(out);
   a.route = route;
   if (route) { a.part_o = at<float>(ws, L.po); a.part_m = at<float>(ws, L.pm); a.part_l = at<float>(ws, L.pl); }
-  int rc = launched(launch_int4_attention(d.kp, a, false, s));
+  uint8_t* img = at<uint8_t>(ws, L.img);
+  a.kv_image = img;
+  int rc = launched(launch_kv_image(d.kp, a, img, s));
+  if (rc != ROTATTN_OK) return rc;
+  rc = launched(launch_int4_attention(d.kp, a, false, s));
   if (rc != ROTATTN_OK) return rc;
   if (fp16_needed) rc = launched(launch_fp16_attention(d.kp, a, false, s));
   return rc;
@@ -343,7 +352,8 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
 
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                        const uint8_t* head_fallback, const int32_t* units, int32_t n_units, int32_t* acc_qk,
-                       int8_t* p_codes, int32_t* acc_pv, float* m_hist, rotattn_stream_t stream) {
+                       int8_t* p_codes, int32_t* acc_pv, float* m_hist, void* workspace, size_t workspace_bytes,
+                       rotattn_stream_t stream) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
@@ -351,6 +361,8 @@ int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, c
   if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
   if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
   if (n_units < 0 || (n_units > 0 && (!units || !acc_qk || !p_codes || !acc_pv || !m_hist))) return ROTATTN_EINVAL;
+  const Layout L = layout(p, d, ROTATTN_CALL_DEBUG_DUMP);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
   if (n_units == 0 || p->L == 0) return ROTATTN_OK;
   AttnArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -362,7 +374,11 @@ int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, c
   a.route = routes(p);
   a.units = units; a.n_units = n_units;
   a.d_acc = acc_qk; a.d_pq = p_codes; a.d_pv = acc_pv; a.d_m = m_hist;
-  return launched(launch_int4_attention(d.kp, a, true, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* img = at<uint8_t>(workspace, L.img);
+  a.kv_image = img;
+  if ((rc = launched(launch_kv_image(d.kp, a, img, s))) != ROTATTN_OK) return rc;
+  return launched(launch_int4_attention(d.kp, a, true, s));
 }
 
 }  // extern "C"

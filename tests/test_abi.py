@@ -37,7 +37,7 @@ def test_exports_match_header():
 
 def test_version_and_strerror():
     lib = _lib()
-    assert lib.rotattn_version() == 1
+    assert lib.rotattn_version() == 2
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.rotattn_strerror(code)
 
@@ -63,9 +63,15 @@ def test_sizes_720p():
     assert s.v_colsum_bytes == 40 * 1182 * 128 * 4
     p2 = Bd.problem_from_workload(W.WORKLOADS["480p"])
     assert Bd.get_sizes(p2).Dp == 192
-    # partial buffers only when block routing is on
-    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == 0
-    assert Bd.workspace_bytes(Bd.problem_from_workload(W.WORKLOADS["mixed"]), Bd.CALL_ATTENTION) > 0
+    # the attention workspace holds one 20480-byte int8 LDS image per (head, key block): 64 K rows of
+    # 128 + 16 bytes, 128 V rows of 64 + 16 bytes and the K scale slot, rounded up to 4096 bytes
+    img = 40 * 1182 * 20480
+    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img
+    assert Bd.workspace_bytes(p, Bd.CALL_DEBUG_DUMP) == img
+    # partial buffers on top only when block routing is on
+    pm = Bd.problem_from_workload(W.WORKLOADS["mixed"])
+    img_m = 12 * 512 * 24576   # D' = 192: 64 x 208 + 128 x 80 + 16 -> 24576
+    assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) >= img_m + 12 * 32768 * 128 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -121,7 +127,11 @@ def test_call_validation_before_launch():
                                     C.c_void_p(good), None, 0, stream) == -4
     # dump with a negative unit count
     assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, -1, None, None, None, None,
-                                  stream) == -1
+                                  None, 0, stream) == -1
+    # dump without its workspace (the K/V block images)
+    one = C.c_void_p(good)
+    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, one, 1, one, one, one, one,
+                                  None, 0, stream) == -4
 
 
 def test_empty_problem_is_a_no_op():
