@@ -35,37 +35,42 @@ namespace rotattn {
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Unpacks 16 packed bytes (32 INT4 codes) into 32 int8 bytes (each code times
-// 16) in the order the matrix-core operands read them, and stores them to LDS.
-__device__ __forceinline__ void store_unpacked(uint8_t* dst, uint4 p) {
-  uint4 a, b;
-  a.x = nib_lo16(p.x); a.y = nib_hi16(p.x); a.z = nib_lo16(p.y); a.w = nib_hi16(p.y);
-  b.x = nib_lo16(p.z); b.y = nib_hi16(p.z); b.z = nib_lo16(p.w); b.w = nib_hi16(p.w);
-  reinterpret_cast<uint4*>(dst)[0] = a;
-  reinterpret_cast<uint4*>(dst)[1] = b;
+// 16) in the order the matrix-core operands read them: the first 16 in lo, the
+// next 16 in hi.
+__device__ __forceinline__ void unpack32(uint4 p, uint4& lo, uint4& hi) {
+  lo.x = nib_lo16(p.x); lo.y = nib_hi16(p.x); lo.z = nib_lo16(p.y); lo.w = nib_hi16(p.y);
+  hi.x = nib_lo16(p.z); hi.y = nib_hi16(p.z); hi.z = nib_lo16(p.w); hi.w = nib_hi16(p.w);
 }
 
 // Expands one (b, h, key block) into the LDS image the attention kernel copies:
 // the packed K codes of its 64 keys and the operand-order V codes of its
-// channels become int8 operands (each code times 16) at their padded LDS
-// offsets, and the K block scale goes into the slot after them. Pad bytes are
-// never read and are left as they are.
+// channels become int8 operands (each code times 16) at their permuted LDS
+// offsets.
 template <int DP, int DV>
 __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_t* __restrict__ k_codes,
-                                                       const float* __restrict__ k_scale,
                                                        const uint8_t* __restrict__ v_codes, uint8_t* image) {
   constexpr int QROW = DP / 2, KPK = kBlock * DP / 2, VPK = DV * 32;
-  constexpr int KROW = kv_krow(DP), VROW = kv_vrow(), KST = kv_kst(DP), IMG = kv_image_bytes(DP, DV);
+  constexpr int KST = kv_kst(DP), IMG = kv_image_bytes(DP, DV);
   const long long u = blockIdx.x;   // (b * H + h) * NB + block
   const long long bh = u / kp.NB;
   const int j = (int)(u - bh * kp.NB);
   uint8_t* dst = image + u * IMG;
   const uint8_t* kg = k_codes + (bh * kp.Lp + (long long)j * kBlock) * QROW;
   const uint8_t* vg = v_codes + u * VPK;
-  for (int o = threadIdx.x * 16; o < KPK; o += 256 * 16)
-    store_unpacked(dst + (o / QROW) * KROW + 2 * (o % QROW), *reinterpret_cast<const uint4*>(kg + o));
-  for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16)
-    store_unpacked(dst + KST + (o >> 5) * VROW + 2 * (o & 31), *reinterpret_cast<const uint4*>(vg + o));
-  if (threadIdx.x == 0) *reinterpret_cast<float4*>(dst + kv_scale_off(DP, DV)) = make_float4(k_scale[u], 0.f, 0.f, 0.f);
+  for (int o = threadIdx.x * 16; o < KPK; o += 256 * 16) {
+    const int r = o / QROW, c = (o - r * QROW) / 8, x = kv_swz(DP, r);   // c: first of the two int8 pieces
+    uint4 lo, hi;
+    unpack32(*reinterpret_cast<const uint4*>(kg + o), lo, hi);
+    *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = lo;
+    *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = hi;
+  }
+  for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16) {
+    const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);
+    uint4 lo, hi;
+    unpack32(*reinterpret_cast<const uint4*>(vg + o), lo, hi);
+    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = lo;
+    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = hi;
+  }
 }
 
 // s_waitcnt that waits until at most N vector-memory operations of this wave
@@ -77,6 +82,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
 }
+// Direct-to-LDS copies: lane l's 16 (or 4) bytes at `src` land at LDS byte
+// address m0 + 16 l (or 4 l). Written as inline asm rather than the builtin so
+// that the compiler does not make LDS reads wait for them: once the stage loop
+// wraps around it can no longer tell which stage a builtin copy writes and
+// waits for every copy in flight. The callers order copies and reads with
+// explicit vmcnt waits and barriers. No register output: the copy writes LDS
+// only, and its address registers are read when it issues. M0 is restored.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void* src, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+
 // Workgroup barrier without a memory fence: LDS stages are filled by
 // direct-to-LDS loads whose completion the caller has already waited for.
 __device__ __forceinline__ void stage_barrier() {
@@ -99,26 +131,34 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   constexpr int NCT = DV / 32;             // 32-channel output tiles
   constexpr int QROW = DP / 2;             // packed code bytes per token
   constexpr int HALF = DP / 4;             // packed code bytes of one lane half
-  constexpr int KROW = kv_krow(DP);        // int8 K row in LDS (padded)
-  constexpr int VROW = kv_vrow();          // int8 V channel row in LDS (padded)
   constexpr int KST = kv_kst(DP);
   constexpr int IMG = kv_image_bytes(DP, DV);   // one LDS stage = one block's image
   constexpr int NDMA = IMG / (NT * 16);    // 16-byte direct-to-LDS loads per thread per block
+  constexpr int NVM = NDMA + 1;            // vector-memory instructions per wave per block (+ the K scale)
   static_assert(IMG % (NT * 16) == 0, "a stage must split evenly over the workgroup");
   static_assert(NST == 3 || NST == 4, "three or four LDS stages");
   // One LDS array per stage, always indexed by a compile-time stage number:
   // the compiler then knows that reads of one stage cannot alias the
   // direct-to-LDS copies into another and does not wait for those copies.
+  // Each stage has a 64-float slot that receives the block's K scale.
   __shared__ __attribute__((aligned(16))) uint8_t stg0[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t stg1[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t stg2[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t stg3[NST == 4 ? IMG : 16];
+  __shared__ float ksc0[64], ksc1[64], ksc2[64], ksc3[64];
   auto stage = [&](auto s_tag) __attribute__((always_inline)) -> uint8_t* {
     constexpr int S = decltype(s_tag)::value;
     if constexpr (S == 0) return stg0;
     else if constexpr (S == 1) return stg1;
     else if constexpr (S == 2) return stg2;
     else return stg3;
+  };
+  auto kscale_slot = [&](auto s_tag) __attribute__((always_inline)) -> float* {
+    constexpr int S = decltype(s_tag)::value;
+    if constexpr (S == 0) return ksc0;
+    else if constexpr (S == 1) return ksc1;
+    else if constexpr (S == 2) return ksc2;
+    else return ksc3;
   };
 
   const int tid = threadIdx.x;
@@ -186,13 +226,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint8_t* img = a.kv_image + (long long)bh * NB * IMG;   // wave-uniform
   const int toff = tid * 16;                                     // this thread's piece of every round
-  auto dma_block = [&](int j, uint8_t* stage_base) __attribute__((always_inline)) {
+  // The K block scale follows in one 4-byte copy per lane (every lane of every
+  // wave copies the same value into the stage's scale slot; no branch, so the
+  // compiler keeps the copy's stage static), so that every wave issues NVM
+  // vector-memory instructions per block.
+  const float* kscale = a.k_scale + (long long)bh * NB;
+  auto dma_block = [&](int j, auto s_tag) __attribute__((always_inline)) {
     const uint8_t* src = img + (long long)j * IMG;
-    uint8_t* dst = stage_base + wave_u * 1024;
+    const uint32_t dst = lds_addr(stage(s_tag)) + wave_u * 1024;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_global_load_lds(src + (toff + i * NT * 16),
-                                       (__attribute__((address_space(3))) void*)(dst + i * NT * 16), 16, 0, 0);
+    for (int i = 0; i < NDMA; ++i) lds_copy16(src + (toff + i * NT * 16), dst + i * NT * 16);
+    lds_copy4(kscale + j, lds_addr(kscale_slot(s_tag)));
   };
 
   // O = o_acc * 2^(m_ref - m_run) + pacc: o_acc holds everything folded so far
@@ -210,6 +254,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
     for (int v = 0; v < 16; ++v) { o_acc[ct][v] = 0.f; pacc[ct][v] = 0; }
 
+  // LDS offsets of this lane's operand pieces: K row `col` (and col + 32, the
+  // same permutation) at logical piece hh*NC + c; V channel row ct*32 + col
+  // (the same permutation for every ct) at logical piece 2*hh + s.
+  int koff[NC], voff[2];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = col * DP + 16 * ((hh * NC + c) ^ kv_swz(DP, col));
+#pragma unroll
+  for (int s = 0; s < 2; ++s) voff[s] = col * 64 + 16 * ((2 * hh + s) ^ kv_swz(64, col));
+
   // S^T (times 256) of the block in `stage`, as two 32-key halves
   v16i s0, s1;
   auto qk = [&](const uint8_t* Ks) __attribute__((always_inline)) {
@@ -217,19 +270,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     for (int v = 0; v < 16; ++v) { s0[v] = 0; s1[v] = 0; }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(Ks + col * KROW + hh * (DP / 2) + 16 * c);
-      const v4i a1 = *reinterpret_cast<const v4i*>(Ks + (32 + col) * KROW + hh * (DP / 2) + 16 * c);
+      const v4i a0 = *reinterpret_cast<const v4i*>(Ks + koff[c]);
+      const v4i a1 = *reinterpret_cast<const v4i*>(Ks + koff[c] + 32 * DP);
       s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qop[c], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qop[c], s1, 0, 0, 0);
     }
   };
 
   // Row max, rescale, P codes and P.V of block j (its S^T is in s0/s1, its V in `stage`).
-  auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, int j) __attribute__((always_inline)) {
+  auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, const float* ksc, int j) __attribute__((always_inline)) {
     constexpr bool kRagged = decltype(ragged_tag)::value;
     const uint8_t* Vs = Ks + KST;
     // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly
-    const float sk = *reinterpret_cast<const float*>(Ks + kv_scale_off(DP, DV));
+    const float sk = ksc[0];
     const float cs = fmul_rn(fmul_rn(cq, sk), 1.0f / 256.0f);
     const int key0 = j * kBlock;
     int mx;
@@ -323,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const v4i vop = *reinterpret_cast<const v4i*>(Vs + (ct * 32 + col) * VROW + 32 * hh + 16 * s);
+        const v4i vop = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[s]);
         pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pop[s], pacc[ct], 0, 0, 0);
       }
     }
@@ -357,12 +410,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  if (q[0] < NB) dma_block(q[0], stage(I0()));
-  if (q[1] < NB) dma_block(q[1], stage(I1()));
-  if (NST == 4 && q[2] < NB) dma_block(q[2], stage(I2()));
+  if (q[0] < NB) dma_block(q[0], I0());
+  if (q[1] < NB) dma_block(q[1], I1());
+  if (NST == 4 && q[2] < NB) dma_block(q[2], I2());
   // q[0] and q[1] must have landed; with four stages q[2] may stay in flight
   if (DUMP || NST == 3 || q[2] >= NB) wait_vmcnt<0>();
-  else wait_vmcnt<NDMA>();
+  else wait_vmcnt<NVM>();
   stage_barrier();
   if (q[0] < NB && work) qk(stage(I0()));
   // one iteration with q[0] in stage S
@@ -371,14 +424,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     using S1 = std::integral_constant<int, (S + 1) % NST>;
     using SL = std::integral_constant<int, (S + NST - 1) % NST>;   // the previous block's stage
     const bool issued = q[NST - 1] < NB;
-    if (issued) dma_block(q[NST - 1], stage(SL()));
+    if (issued) dma_block(q[NST - 1], SL());
     if (work) {
-      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), q[0]);
+      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
       qk(stage(S1()));   // stale data when there is no next block: computed, never used
     }
     // q[2] must have landed before the next iteration reads it
     if (DUMP || NST == 3 || !issued) wait_vmcnt<0>();
-    else wait_vmcnt<NDMA>();
+    else wait_vmcnt<NVM>();
     stage_barrier();
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i) q[i] = q[i + 1];
@@ -401,7 +454,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   if (j < NB && work) {
     wait_vmcnt<0>();
     const uint8_t* Ks = st == 0 ? stage(I0()) : st == 1 ? stage(I1()) : st == 2 ? stage(I2()) : stage(I3());
-    softmax_pv(std::integral_constant<bool, true>(), Ks, j);
+    const float* ksc = st == 0 ? ksc0 : st == 1 ? ksc1 : st == 2 ? ksc2 : ksc3;
+    softmax_pv(std::integral_constant<bool, true>(), Ks, ksc, j);
   }
 
   if (DUMP || !work) return;
@@ -459,7 +513,7 @@ template <int DP, int DV>
 struct Shape {
   static constexpr int kWaves = 4;
   // two workgroups' rings plus a few hundred bytes of other LDS must fit in 160 KB
-  static constexpr int kStages = (2 * 4 * kv_image_bytes(DP, DV) + 1024 <= 160 * 1024) ? 4 : 3;
+  static constexpr int kStages = (2 * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3;
   static constexpr int kOcc = 2;
 };
 
@@ -482,8 +536,8 @@ static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump
 template <int DP, int DV>
 static hipError_t launch_kv_image_t(const KProblem& kp, const AttnArgs& a, uint8_t* image, hipStream_t s) {
   const long long units = (long long)kp.B * kp.H * kp.NB;
-  hipLaunchKernelGGL((kv_image_kernel<DP, DV>), dim3((unsigned)units), dim3(256), 0, s, kp, a.k_codes, a.k_scale,
-                     a.v_codes, image);
+  hipLaunchKernelGGL((kv_image_kernel<DP, DV>), dim3((unsigned)units), dim3(256), 0, s, kp, a.k_codes, a.v_codes,
+                     image);
   return hipGetLastError();
 }
 

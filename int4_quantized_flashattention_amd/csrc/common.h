@@ -50,16 +50,16 @@ __device__ __forceinline__ v4i unpack16(uint2 p) {
 
 // LDS stage of one 64-key block in the INT4 attention kernel, and the byte image
 // of it in HBM that the kernel copies with direct-to-LDS loads: 64 K rows of DP
-// int8 operand bytes padded to DP + 16 (against bank conflicts), then DV V
-// channel rows of 64 int8 operand bytes padded to 80, then the K block scale in
-// a 16-byte slot; the whole rounded up to a multiple of 4096 bytes so that every
-// thread of a 256-thread workgroup copies the same number of 16-byte pieces.
-__host__ __device__ constexpr int kv_krow(int DP) { return DP + 16; }
-__host__ __device__ constexpr int kv_vrow() { return 64 + 16; }
-__host__ __device__ constexpr int kv_kst(int DP) { return kBlock * kv_krow(DP); }
-__host__ __device__ constexpr int kv_scale_off(int DP, int DV) { return kv_kst(DP) + DV * kv_vrow(); }
-__host__ __device__ constexpr int kv_image_bytes(int DP, int DV) {
-  return (kv_scale_off(DP, DV) + 16 + 4095) / 4096 * 4096;
+// int8 operand bytes, then DV V channel rows of 64 int8 operand bytes. Within a
+// row the 16-byte pieces are permuted by kv_swz so that 8 or 16 consecutive
+// rows read at the same logical piece fall in distinct LDS banks. Every size is
+// a multiple of 4096 bytes, so each thread of a 256-thread workgroup copies the
+// same number of 16-byte pieces.
+__host__ __device__ constexpr int kv_kst(int DP) { return kBlock * DP; }
+__host__ __device__ constexpr int kv_image_bytes(int DP, int DV) { return kBlock * DP + DV * 64; }
+// physical piece of logical 16-byte piece c in row r: c ^ kv_swz(row bytes, r)
+__host__ __device__ constexpr int kv_swz(int row_bytes, int r) {
+  return row_bytes == 128 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -63,14 +63,14 @@ def test_sizes_720p():
     assert s.v_colsum_bytes == 40 * 1182 * 128 * 4
     p2 = Bd.problem_from_workload(W.WORKLOADS["480p"])
     assert Bd.get_sizes(p2).Dp == 192
-    # the attention workspace holds one 20480-byte int8 LDS image per (head, key block): 64 K rows of
-    # 128 + 16 bytes, 128 V rows of 64 + 16 bytes and the K scale slot, rounded up to 4096 bytes
-    img = 40 * 1182 * 20480
+    # the attention workspace holds one 16384-byte int8 LDS image per (head, key block): 64 K rows of
+    # 128 bytes and 128 V rows of 64 bytes
+    img = 40 * 1182 * 16384
     assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img
     assert Bd.workspace_bytes(p, Bd.CALL_DEBUG_DUMP) == img
     # partial buffers on top only when block routing is on
     pm = Bd.problem_from_workload(W.WORKLOADS["mixed"])
-    img_m = 12 * 512 * 24576   # D' = 192: 64 x 208 + 128 x 80 + 16 -> 24576
+    img_m = 12 * 512 * 20480   # D' = 192: 64 x 192 + 128 x 64
     assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) >= img_m + 12 * 32768 * 128 * 4
 
 
