@@ -10,21 +10,23 @@
 // order; tiles routed to the FP16 path are skipped like masked blocks.
 //
 // Layout of the work (one workgroup = 4 waves = 128 query rows of one head):
-//  * S^T = K Q^T with v_mfma_i32_32x32x32_i8: K codes are the A operand (rows
-//    = keys), Q codes the B operand (columns = queries). Each lane then owns
+//  * S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 on E4M3 operands: the INT4
+//    codes are exact in E4M3 and the float32 sums of their products are exact
+//    integers, so this is the integer Q.K^T, delivered as floats (no
+//    int-to-float conversion per score). K codes are the A operand (rows =
+//    keys), Q codes the B operand (columns = queries). Each lane then owns
 //    one query column and 16 of the 32 keys of a 32 x 32 tile, so the row
 //    max and row sum are in-lane plus one exchange with lane ^ 32, and the P
 //    codes are already laid out as the B operand of the next product.
-//  * O^T = V^T P^T with the same instruction: V codes (A, rows = channels,
-//    stored by the V quantizer in exactly this operand order) times the P
-//    codes (B). The zero-point correction is applied inside the product: the
+//  * O^T = V^T P^T with v_mfma_i32_32x32x32_i8: V codes (A, rows = channels,
+//    stored by the V quantizer in exactly this operand order; int8, each code
+//    times 16, the factor folded into the output scale) times the P codes
+//    (B). The zero-point correction is applied inside the product: the
 //    kernel feeds the shifted code pq + 8 = rne(15 P) in [0, 15], and
 //    sum (pq + 8) v = sum pq v + 8 colsum(v) exactly (integer identity).
-//  * INT4 nibbles become int8 operands with two ANDs and a shift per 8 codes
-//    (each value times 16; the factors 256 and 16 are folded into the float
-//    scales exactly).
-//  * K and V tiles of the current key block are staged through LDS once per
-//    workgroup.
+//  * A pre-pass expands each key block once into the exact LDS image of one
+//    pipeline stage (E4M3 K rows, int8 V rows); the loop copies images into
+//    LDS with direct-to-LDS loads, four stages deep where LDS allows.
 #include "common.h"
 
 #include <climits>
@@ -42,10 +44,40 @@ __device__ __forceinline__ void unpack32(uint4 p, uint4& lo, uint4& hi) {
   hi.x = nib_lo16(p.z); hi.y = nib_hi16(p.z); hi.z = nib_lo16(p.w); hi.w = nib_hi16(p.w);
 }
 
+// FP8 E4M3 byte of a 4-bit two's-complement code in [-8, 7]: every such
+// integer is exact in E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits),
+// so the FP8 matrix cores multiply the codes exactly, and their float32 sums over
+// at most 192 products of magnitude <= 49 are exact integers.
+__device__ __forceinline__ uint32_t e4m3_of_code(uint32_t nib) {
+  const uint32_t mag = (nib & 8u) ? 16u - nib : nib;   // 0..8
+  const uint32_t byte = ((uint32_t)(0x4E4C4A4844403800ull >> (8 * (mag & 7u))) & 0xFFu) | (mag == 8u ? 0x50u : 0u);
+  return byte | ((nib & 8u) ? 0x80u : 0u);
+}
+// 16 packed bytes (32 codes, dim 2i in the low nibble of byte i) -> 32 E4M3 bytes in dim order
+__device__ __forceinline__ void e4m3_expand32(uint4 p, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = 0, b = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {   // packed bytes 2k, 2k+1 of word i -> 4 output bytes each
+      const uint32_t b0 = (w[i] >> (16 * k)) & 0xFFu, b1 = (w[i] >> (16 * k + 8)) & 0xFFu;
+      const uint32_t v = e4m3_of_code(b0 & 15u) | (e4m3_of_code(b0 >> 4) << 8) | (e4m3_of_code(b1 & 15u) << 16) |
+                         (e4m3_of_code(b1 >> 4) << 24);
+      if (k == 0) a = v; else b = v;
+    }
+    o[2 * i] = a;
+    o[2 * i + 1] = b;
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // Expands one (b, h, key block) into the LDS image the attention kernel copies:
-// the packed K codes of its 64 keys and the operand-order V codes of its
-// channels become int8 operands (each code times 16) at their permuted LDS
-// offsets.
+// the packed K codes of its 64 keys become E4M3 bytes in dim order, and the
+// operand-order V codes of its channels int8 operands (each code times 16), all
+// at their permuted LDS offsets.
 template <int DP, int DV>
 __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_t* __restrict__ k_codes,
                                                        const uint8_t* __restrict__ v_codes, uint8_t* image) {
@@ -60,7 +92,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
   for (int o = threadIdx.x * 16; o < KPK; o += 256 * 16) {
     const int r = o / QROW, c = (o - r * QROW) / 8, x = kv_swz(DP, r);   // c: first of the two int8 pieces
     uint4 lo, hi;
-    unpack32(*reinterpret_cast<const uint4*>(kg + o), lo, hi);
+    e4m3_expand32(*reinterpret_cast<const uint4*>(kg + o), lo, hi);
     *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = lo;
     *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = hi;
   }
@@ -127,10 +159,9 @@ __device__ __forceinline__ void stage_barrier() {
 template <int DP, int DV, int NW, int NST, int OCC, bool DUMP>
 __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
-  constexpr int NC = DP / 32;              // 32-deep slices of the rotated head dim
+  constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP8 product each)
   constexpr int NCT = DV / 32;             // 32-channel output tiles
   constexpr int QROW = DP / 2;             // packed code bytes per token
-  constexpr int HALF = DP / 4;             // packed code bytes of one lane half
   constexpr int KST = kv_kst(DP);
   constexpr int IMG = kv_image_bytes(DP, DV);   // one LDS stage = one block's image
   constexpr int NDMA = IMG / (NT * 16);    // 16-byte direct-to-LDS loads per thread per block
@@ -202,13 +233,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   const bool mixed = work && a.route && a.head_kflag[bh] != 0;
   if (!__syncthreads_or(work)) return;
 
-  // Q codes of this lane's query (column) and half of the rotated dims.
-  v4i qop[NC];
+  // Q codes of this lane's query (column) as E4M3: slice c, lane half hh holds
+  // dims [64 c + 32 hh, +32) (the K rows are read with the same split).
+  v8i qop[NC];
   float cq = 0.f;
   if (work) {
-    const uint8_t* qrow = a.q_codes + ((long long)bh * Lp + wrow + col) * QROW + hh * HALF;
+    const uint8_t* qrow = a.q_codes + ((long long)bh * Lp + wrow + col) * QROW;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qop[c] = unpack16(*reinterpret_cast<const uint2*>(qrow + 8 * c));
+    for (int c = 0; c < NC; ++c) {
+      uint4 lo, hi;
+      e4m3_expand32(*reinterpret_cast<const uint4*>(qrow + 32 * c + 16 * hh), lo, hi);
+      qop[c] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
     cq = fmul_rn(a.q_scale[bh * NB + qblk], c0);
   }
 
@@ -255,25 +291,31 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     for (int v = 0; v < 16; ++v) { o_acc[ct][v] = 0.f; pacc[ct][v] = 0; }
 
   // LDS offsets of this lane's operand pieces: K row `col` (and col + 32, the
-  // same permutation) at logical piece hh*NC + c; V channel row ct*32 + col
-  // (the same permutation for every ct) at logical piece 2*hh + s.
-  int koff[NC], voff[2];
+  // same permutation) at logical pieces 4c + 2hh and 4c + 2hh + 1 (dims
+  // [64 c + 32 hh, +32)); V channel row ct*32 + col (the same permutation for
+  // every ct) at logical piece 2*hh + s.
+  int koff[2 * NC], voff[2];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) koff[c] = col * DP + 16 * ((hh * NC + c) ^ kv_swz(DP, col));
+  for (int c = 0; c < 2 * NC; ++c) koff[c] = col * DP + 16 * ((4 * (c >> 1) + 2 * hh + (c & 1)) ^ kv_swz(DP, col));
 #pragma unroll
   for (int s = 0; s < 2; ++s) voff[s] = col * 64 + 16 * ((2 * hh + s) ^ kv_swz(64, col));
 
-  // S^T (times 256) of the block in `stage`, as two 32-key halves
-  v16i s0, s1;
+  // S^T of the block in `stage` (the integer q.k as exact floats), as two
+  // 32-key halves, on the FP8 matrix cores (E4M3 codes, no block scaling)
+  v16f s0, s1;
   auto qk = [&](const uint8_t* Ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0; s1[v] = 0; }
+    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(Ks + koff[c]);
-      const v4i a1 = *reinterpret_cast<const v4i*>(Ks + koff[c] + 32 * DP);
-      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qop[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qop[c], s1, 0, 0, 0);
+      const v4i a0l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c]);
+      const v4i a0h = *reinterpret_cast<const v4i*>(Ks + koff[2 * c + 1]);
+      const v4i a1l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c] + 32 * DP);
+      const v4i a1h = *reinterpret_cast<const v4i*>(Ks + koff[2 * c + 1] + 32 * DP);
+      const v8i a0 = v8i{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
+      const v8i a1 = v8i{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], s0, 0, 0, 0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[c], s1, 0, 0, 0, 0, 0, 0);
     }
   };
 
@@ -281,35 +323,35 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, const float* ksc, int j) __attribute__((always_inline)) {
     constexpr bool kRagged = decltype(ragged_tag)::value;
     const uint8_t* Vs = Ks + KST;
-    // c = float(float(sq c0) sk); the operands carry a factor 256, folded in exactly
+    // c = float(float(sq c0) sk)
     const float sk = ksc[0];
-    const float cs = fmul_rn(fmul_rn(cq, sk), 1.0f / 256.0f);
+    const float cs = fmul_rn(cq, sk);
     const int key0 = j * kBlock;
-    int mx;
+    float mx;
     if (!kRagged) {
       // two interleaved max3 chains over the 32 values of this lane
-      int ma = max(s0[0], s1[0]), mb = max(s0[1], s1[1]);
+      float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
 #pragma unroll
       for (int v = 2; v < 16; v += 2) {
-        ma = max(max(ma, s0[v]), s1[v]);
-        mb = max(max(mb, s0[v + 1]), s1[v + 1]);
+        ma = fmaxf(fmaxf(ma, s0[v]), s1[v]);
+        mb = fmaxf(fmaxf(mb, s0[v + 1]), s1[v + 1]);
       }
-      mx = max(ma, mb);
+      mx = fmaxf(ma, mb);
     } else {
-      mx = INT_MIN;
+      mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int k0 = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (k0 < L) mx = max(mx, s0[v]);
-        if (k0 + 32 < L) mx = max(mx, s1[v]);
+        if (k0 < L) mx = fmaxf(mx, s0[v]);
+        if (k0 + 32 < L) mx = fmaxf(mx, s1[v]);
       }
     }
     {  // the other 32 keys of this query sit in lane ^ 32
-      const auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
-      mx = max((int)sw[0], (int)sw[1]);   // the builtin yields unsigned lanes: compare as signed
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    // max over the block of float(acc) * c = float(max acc) * c, as c >= 0
-    const float m_new = fmaxf(m_run, fmul_rn((float)mx, cs));
+    // max over the block of acc * c = (max acc) * c, as c >= 0 (acc is an exact integer)
+    const float m_new = fmaxf(m_run, fmul_rn(mx, cs));
     const bool flush = DUMP || __ballot(m_new > m_run) != 0ull;
     if (flush) {
       // fold pacc (at m_run) into o_acc (at m_ref); nothing folded yet before the first block
@@ -353,7 +395,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int v = 4 * kq + bb;
-          float t = fmaf((float)(s == 0 ? s0[v] : s1[v]), cs, nm15);
+          float t = fmaf(s == 0 ? s0[v] : s1[v], cs, nm15);
           if (kRagged) {
             const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
             if (key >= L) t = -INFINITY;
@@ -364,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
           if (DUMP && wrow + col < L) {
             const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
             const long long di = ((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key;
-            a.d_acc[di] = (s == 0 ? s0[v] : s1[v]) >> 8;
+            a.d_acc[di] = (int)(s == 0 ? s0[v] : s1[v]);
             a.d_pq[di] = (int8_t)((int)((word >> (8 * bb)) & 0xFFu) - 8);
           }
         }
