@@ -156,7 +156,7 @@ __device__ __forceinline__ void stage_barrier() {
 // matrix cores. O is accumulated in int32 by the matrix cores and folded into
 // the float32 accumulator only when some row max of the wave grows (the
 // rescale factor is exactly 1 otherwise).
-template <int DP, int DV, int NW, int NST, int OCC, bool DUMP>
+template <int DP, int DV, int NW, int NST, int OCC, bool EARLY, bool DUMP>
 __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
   constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP8 product each)
@@ -302,10 +302,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 
   // S^T of the block in `stage` (the integer q.k as exact floats), as two
   // 32-key halves, on the FP8 matrix cores (E4M3 codes, no block scaling)
-  v16f s0, s1;
-  auto qk = [&](const uint8_t* Ks) __attribute__((always_inline)) {
+  v16f s0, s1;   // S^T of the block in the softmax
+  v16f n0, n1;   // S^T of the next block, on the matrix cores meanwhile
+  auto qk = [&](const uint8_t* Ks, v16f& d0, v16f& d1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+    for (int v = 0; v < 16; ++v) { d0[v] = 0.f; d1[v] = 0.f; }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const v4i a0l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c]);
@@ -314,8 +315,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       const v4i a1h = *reinterpret_cast<const v4i*>(Ks + koff[2 * c + 1] + 32 * DP);
       const v8i a0 = v8i{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
       const v8i a1 = v8i{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
-      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], s0, 0, 0, 0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[c], s1, 0, 0, 0, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], d0, 0, 0, 0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[c], d1, 0, 0, 0, 0, 0, 0);
     }
   };
 
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   if (DUMP || NST == 3 || q[2] >= NB) wait_vmcnt<0>();
   else wait_vmcnt<NVM>();
   stage_barrier();
-  if (q[0] < NB && work) qk(stage(I0()));
+  if (q[0] < NB && work) qk(stage(I0()), s0, s1);
   // one iteration with q[0] in stage S
   auto iter = [&](auto s_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(s_tag)::value;
@@ -468,8 +469,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     const bool issued = q[NST - 1] < NB;
     if (issued) dma_block(q[NST - 1], SL());
     if (work) {
-      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
-      qk(stage(S1()));   // stale data when there is no next block: computed, never used
+      // S^T of the next block (stale data when there is no next block:
+      // computed, never used). EARLY issues it before this block's softmax,
+      // into a second register set, so the matrix cores work on it meanwhile.
+      if constexpr (EARLY) {
+        qk(stage(S1()), n0, n1);
+        softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
+        s0 = n0;
+        s1 = n1;
+      } else {
+        softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
+        qk(stage(S1()), s0, s1);
+      }
     }
     // q[2] must have landed before the next iteration reads it
     if (DUMP || NST == 3 || !issued) wait_vmcnt<0>();
@@ -557,6 +568,9 @@ struct Shape {
   // two workgroups' rings plus a few hundred bytes of other LDS must fit in 160 KB
   static constexpr int kStages = (2 * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3;
   static constexpr int kOcc = 2;
+  // next block's S^T issued before the softmax (32 more registers): where the
+  // register file still holds two waves per SIMD without spilling
+  static constexpr bool kEarly = (DP == 128);
 };
 
 template <int DP, int DV>
@@ -564,13 +578,14 @@ static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump
                                 hipStream_t s) {
   using S = Shape<DP, DV>;
   constexpr int W = S::kWaves, NS = S::kStages, OC = S::kOcc;
+  constexpr bool E = S::kEarly;
   if (dump) {
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true>), dim3(a.n_units), dim3(W * 64), 0, s, kp, a,
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, E, true>), dim3(a.n_units), dim3(W * 64), 0, s, kp, a,
                        c0, l15);
   } else {
     const int ntiles = (kp.L + 32 * W - 1) / (32 * W);
     dim3 grid(ntiles * kp.H * kp.B);
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false>), grid, dim3(W * 64), 0, s, kp, a, c0, l15);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, E, false>), grid, dim3(W * 64), 0, s, kp, a, c0, l15);
   }
   return hipGetLastError();
 }
