@@ -18,12 +18,14 @@
 //    one query column and 16 of the 32 keys of a 32 x 32 tile, so the row
 //    max and row sum are in-lane plus one exchange with lane ^ 32, and the P
 //    codes are already laid out as the B operand of the next product.
-//  * O^T = V^T P^T with v_mfma_i32_32x32x32_i8: V codes (A, rows = channels,
-//    stored by the V quantizer in exactly this operand order; int8, each code
-//    times 16, the factor folded into the output scale) times the P codes
-//    (B). The zero-point correction is applied inside the product: the
-//    kernel feeds the shifted code pq + 8 = rne(15 P) in [0, 15], and
-//    sum (pq + 8) v = sum pq v + 8 colsum(v) exactly (integer identity).
+//  * O^T = V^T P^T with the same FP8 instruction: V codes (A, rows = channels,
+//    stored by the V quantizer in exactly this operand order) as E4M3, times
+//    the P code bytes pq + 8 = rne(15 P) in [0, 15] as produced by
+//    v_cvt_pk_u8_f32 (B): read as E4M3 such a byte n is exactly n * 2^-9, so
+//    the float32 result is 2^-9 sum (pq + 8) v, exact; the zero-point
+//    correction rides inside it, as sum (pq + 8) v = sum pq v + 8 colsum(v)
+//    (integer identity). The float accumulator is rescaled in place when a
+//    row max grows.
 //  * A pre-pass expands each key block once into the exact LDS image of one
 //    pipeline stage (E4M3 K rows, int8 V rows); the loop copies images into
 //    LDS with direct-to-LDS loads, four stages deep where LDS allows.
@@ -35,14 +37,6 @@
 namespace rotattn {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Unpacks 16 packed bytes (32 INT4 codes) into 32 int8 bytes (each code times
-// 16) in the order the matrix-core operands read them: the first 16 in lo, the
-// next 16 in hi.
-__device__ __forceinline__ void unpack32(uint4 p, uint4& lo, uint4& hi) {
-  lo.x = nib_lo16(p.x); lo.y = nib_hi16(p.x); lo.z = nib_lo16(p.y); lo.w = nib_hi16(p.y);
-  hi.x = nib_lo16(p.z); hi.y = nib_hi16(p.z); hi.z = nib_lo16(p.w); hi.w = nib_hi16(p.w);
-}
 
 // FP8 E4M3 byte of a 4-bit two's-complement code in [-8, 7]: every such
 // integer is exact in E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits),
@@ -74,10 +68,31 @@ __device__ __forceinline__ void e4m3_expand32(uint4 p, uint4& lo, uint4& hi) {
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// 16 packed bytes in the operand order of the V codes (for each 4-byte word: the
+// four low nibbles, then the four high nibbles) -> 32 E4M3 bytes in that order
+__device__ __forceinline__ void e4m3_expand32_split(uint4 p, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t l = 0, h = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (w[i] >> (8 * b)) & 0xFFu;
+      l |= e4m3_of_code(byte & 15u) << (8 * b);
+      h |= e4m3_of_code(byte >> 4) << (8 * b);
+    }
+    o[2 * i] = l;
+    o[2 * i + 1] = h;
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // Expands one (b, h, key block) into the LDS image the attention kernel copies:
 // the packed K codes of its 64 keys become E4M3 bytes in dim order, and the
-// operand-order V codes of its channels int8 operands (each code times 16), all
-// at their permuted LDS offsets.
+// operand-order V codes of its channels E4M3 bytes in the same operand order,
+// all at their permuted LDS offsets.
 template <int DP, int DV>
 __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_t* __restrict__ k_codes,
                                                        const uint8_t* __restrict__ v_codes, uint8_t* image) {
@@ -99,7 +114,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
   for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16) {
     const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);
     uint4 lo, hi;
-    unpack32(*reinterpret_cast<const uint4*>(vg + o), lo, hi);
+    e4m3_expand32_split(*reinterpret_cast<const uint4*>(vg + o), lo, hi);
     *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = lo;
     *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = hi;
   }
@@ -275,20 +290,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     lds_copy4(kscale + j, lds_addr(kscale_slot(s_tag)));
   };
 
-  // O = o_acc * 2^(m_ref - m_run) + pacc: o_acc holds everything folded so far
-  // at a fixed reference max m_ref (per row), pacc the int32 sum since the
-  // last fold at the current running max m_run. A fold is one multiply-add
-  // per value and leaves o_acc unscaled; the reference moves only when
-  // m_run - m_ref exceeds 64 (to keep o_acc far from overflow).
+  // O^T accumulates on the FP8 matrix cores in float32. The V codes are E4M3
+  // (exact integers), and the P code byte n = pq + 8 that v_cvt_pk_u8_f32
+  // produces, read as E4M3, is exactly n * 2^-9 (a subnormal below 8), so each
+  // block adds 2^-9 * sum (pq + 8) v exactly. o is kept at the running max:
+  // when a row max of the wave grows it is rescaled in place.
   float m_run = -INFINITY;
-  float m_ref = -INFINITY;
   float l15 = 0.f;                 // row sum of 15 P (lane-partial), at m_run
-  v16f o_acc[NCT];                 // float32 O (times 16) at m_ref
-  v16i pacc[NCT];                  // int32 O (times 16) at m_run since the last fold
+  v16f o[NCT];                     // 2^-9 * sum (pq + 8) v, at m_run
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { o_acc[ct][v] = 0.f; pacc[ct][v] = 0; }
+    for (int v = 0; v < 16; ++v) o[ct][v] = 0.f;
 
   // LDS offsets of this lane's operand pieces: K row `col` (and col + 32, the
   // same permutation) at logical pieces 4c + 2hh and 4c + 2hh + 1 (dims
@@ -355,34 +368,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     const float m_new = fmaxf(m_run, fmul_rn(mx, cs));
     const bool flush = DUMP || __ballot(m_new > m_run) != 0ull;
     if (flush) {
-      // fold pacc (at m_run) into o_acc (at m_ref); nothing folded yet before the first block
-      const bool first = m_run == -INFINITY;
-      const float g = first ? 0.f : exp2_hw(fsub_rn(m_run, m_ref));
-      m_ref = first ? m_new : m_ref;
+      // alpha = 2^(m_old - m_new): 0 before the first block, 1 where the row max did not grow
+      const float alpha = exp2_hw(fsub_rn(m_run, m_new));
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o_acc[ct][v] = fmaf((float)pacc[ct][v], g, o_acc[ct][v]);
-      {  // zero the int32 accumulators on the matrix cores (0 x 0 + 0)
-        v4i z4;
-        v16i z16;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) z4[v] = 0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) z16[v] = 0;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(z4, z4, z16, 0, 0, 0);
-      }
-      l15 *= exp2_hw(fsub_rn(m_run, m_new));
+        for (int v = 0; v < 16; ++v) o[ct][v] *= alpha;
+      l15 *= alpha;
       m_run = m_new;
-      if (__ballot(fsub_rn(m_run, m_ref) > 64.f) != 0ull) {
-        const float f = exp2_hw(fsub_rn(m_ref, m_run));
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o_acc[ct][v] *= f;
-        m_ref = m_run;
-      }
     }
     // 15 P = 2^(acc c - (m - log2 15)); its rne is pq + 8, packed by v_cvt_pk_u8_f32
     const float nm15 = -fsub_rn(m_run, log2_15);
@@ -415,25 +408,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       }
     l15 += ls0 + ls1;
     // O^T += V^T (pq + 8)^T: the zero-point correction rides inside the product
+    const v8i pb = v8i{pop[0][0], pop[0][1], pop[0][2], pop[0][3], pop[1][0], pop[1][1], pop[1][2], pop[1][3]};
+    const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
+      const v4i vl = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[0]);
+      const v4i vh = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[1]);
+      const v8i va = v8i{vl[0], vl[1], vl[2], vl[3], vh[0], vh[1], vh[2], vh[3]};
+      if constexpr (DUMP) {
+        // this block's sum alone, to expose the integers sum (pq + 8) v
+        v16f z;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const v4i vop = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[s]);
-        pacc[ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pop[s], pacc[ct], 0, 0, 0);
-      }
-    }
-    if (DUMP && wrow + col < L) {
-      const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int v = 0; v < 16; ++v) z[v] = 0.f;
+        const v16f blk = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int ch = ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          a.d_pv[(r * NB + j) * DV + ch] = pacc[ct][v] >> 4;
+          o[ct][v] += blk[v];
+          if (wrow + col < L) {
+            const int ch = ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            a.d_pv[(r * NB + j) * DV + ch] = (int)(blk[v] * 512.0f);
+          }
         }
-      if (hh == 0) a.d_m[r * NB + j] = m_run;
+      } else {
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[ct], 0, 0, 0, 0, 0, 0);
+      }
     }
+    if (DUMP && wrow + col < L && hh == 0) a.d_m[r * NB + j] = m_run;
   };
 
   // Software pipeline over the key blocks this path takes (ascending), with an
@@ -512,20 +512,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   }
 
   if (DUMP || !work) return;
-  {  // O = o_acc 2^(m_ref - m_run) + pacc
-    const float f = (m_run == -INFINITY) ? 0.f : exp2_hw(fsub_rn(m_ref, m_run));
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o_acc[ct][v] = fmaf(o_acc[ct][v], f, (float)pacc[ct][v]);
-  }
   const float l15t = l15 + __shfl_xor(l15, 32);
   const int row = wrow + col;
   if (row >= L) return;
   const float* svp = a.v_scale + (long long)bh * DV;
   if (!mixed) {
-    // out = O (s_v / 15) / l with O = o/16 and l = l15/15
-    const float inv = 1.0f / (16.0f * l15t);
+    // out = O (s_v / 15) / l with O = 2^9 o and l = l15 / 15
+    const float inv = 512.0f / l15t;
     __half* orow = a.out + (long long)b * kp.sb + (long long)h * kp.sh + (long long)row * kp.sl;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -534,7 +527,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
         const int ch = ct * 32 + 8 * g + 4 * hh;
         __half hv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn(o_acc[ct][4 * g + e] * svp[ch + e] * inv);
+        for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn(o[ct][4 * g + e] * svp[ch + e] * inv);
         *reinterpret_cast<uint2*>(orow + ch) = *reinterpret_cast<const uint2*>(hv);
       }
   } else {
@@ -545,10 +538,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       for (int g = 0; g < 4; ++g) {
         const int ch = ct * 32 + 8 * g + 4 * hh;
         float4 f;
-        f.x = o_acc[ct][4 * g + 0] * (svp[ch + 0] * (1.0f / 240.0f));
-        f.y = o_acc[ct][4 * g + 1] * (svp[ch + 1] * (1.0f / 240.0f));
-        f.z = o_acc[ct][4 * g + 2] * (svp[ch + 2] * (1.0f / 240.0f));
-        f.w = o_acc[ct][4 * g + 3] * (svp[ch + 3] * (1.0f / 240.0f));
+        // O (s_v / 15) with O = 2^9 o
+        f.x = o[ct][4 * g + 0] * (svp[ch + 0] * (512.0f / 15.0f));
+        f.y = o[ct][4 * g + 1] * (svp[ch + 1] * (512.0f / 15.0f));
+        f.z = o[ct][4 * g + 2] * (svp[ch + 2] * (512.0f / 15.0f));
+        f.w = o[ct][4 * g + 3] * (svp[ch + 3] * (512.0f / 15.0f));
         *reinterpret_cast<float4*>(po + ch) = f;
       }
     if (hh == 0) {
