@@ -377,7 +377,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       l15 *= alpha;
       m_run = m_new;
     }
-    // 15 P = 2^(acc c - (m - log2 15)); its rne is pq + 8, packed by v_cvt_pk_u8_f32
+    // 15 P = 2^(acc c - (m - log2 15)); its rne is the code byte pq + 8. Two
+    // codes per instruction: v_cvt_scalef32_pk_fp8_f32 converts 15P / 2^9 to
+    // E4M3, whose grid below 2^-5 is exactly the multiples of 2^-9, so with
+    // round-to-nearest-even the byte is rne(15P) (the E4M3 bit pattern of
+    // n * 2^-9 is n for n < 16) -- the same byte v_cvt_pk_u8_f32 gives.
     const float nm15 = -fsub_rn(m_run, log2_15);
     v4i pop[2];
     float ls0 = 0.f, ls1 = 0.f;
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
-        uint32_t word = 0;
+        float p15[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int v = 4 * kq + bb;
@@ -394,10 +398,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
             const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
             if (key >= L) t = -INFINITY;
           }
-          const float p15 = exp2_hw(t);
-          if (bb & 1) ls1 += p15; else ls0 += p15;
-          word = __builtin_amdgcn_cvt_pk_u8_f32(p15, bb, word);
-          if (DUMP && wrow + col < L) {
+          p15[bb] = exp2_hw(t);
+          if (bb & 1) ls1 += p15[bb]; else ls0 += p15[bb];
+        }
+        // both halves of w are written below, so its initial value does not
+        // matter: an empty asm defines the register without an instruction
+        v2s16 w;
+        asm volatile("" : "=v"(w));
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p15[0], p15[1], 512.0f, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p15[2], p15[3], 512.0f, true);
+        const uint32_t word = (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
+        if (DUMP && wrow + col < L) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int v = 4 * kq + bb;
             const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
             const long long di = ((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key;
             a.d_acc[di] = (int)(s == 0 ? s0[v] : s1[v]);

@@ -14,6 +14,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v2s16 __attribute__((ext_vector_type(2)));
 
 // Everything a kernel needs to know about the problem, passed by value.
 struct KProblem {
