@@ -8,7 +8,8 @@ rotattn_quantize_v (per-channel INT4 V + column sums) -> rotattn_attention
 Metric: attention TOPS = 4 B H L^2 D / step time (D the nominal head dim),
 on the 720p-style workload (B=1, H=40, L=75600, D=128). The roofline entry
 reports the INT4 attention kernel alone against the INT8 matrix-core peak
-(5.0 POP/s dense). The CPU baseline is the oracle (numpy) on a bounded
+(5.0 POP/s dense; the INT4 codes are multiplied exactly on the FP8 matrix path,
+whose dense peak is the same). The CPU baseline is the oracle (numpy) on a bounded
 sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
@@ -173,7 +174,7 @@ def main():
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "i4", "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} L={w.L} D={w.D} grid={'x'.join(map(str, w.grid))} "
                                f"prefix={w.prefix} rotation={'group64' if w.rotation else 'full'}",
                    "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.D, "parallelism": "none"},
