@@ -47,25 +47,26 @@ __device__ __forceinline__ uint32_t e4m3_of_code(uint32_t nib) {
   const uint32_t byte = ((uint32_t)(0x4E4C4A4844403800ull >> (8 * (mag & 7u))) & 0xFFu) | (mag == 8u ? 0x50u : 0u);
   return byte | ((nib & 8u) ? 0x80u : 0u);
 }
-// 16 packed bytes (32 codes, dim 2i in the low nibble of byte i) -> 32 E4M3 bytes in dim order
-__device__ __forceinline__ void e4m3_expand32(uint4 p, uint4& lo, uint4& hi) {
+// FP6 E2M3 bits (sign, 2 exponent bits with bias 1, 3 mantissa bits) of a
+// 4-bit two's-complement code in [-7, 7]: every such integer is exact in E2M3
+// (7 = 1.75 * 2^2), so the FP6 matrix path also multiplies the codes exactly.
+__device__ __forceinline__ uint32_t e2m3_of_code(uint32_t nib) {
+  const uint32_t mag = ((nib & 8u) ? 16u - nib : nib) & 7u;   // -8 never occurs for Q/K codes
+  return ((uint32_t)(0x1E1C1A1814100800ull >> (8 * mag)) & 0x3Fu) | ((nib & 8u) ? 0x20u : 0u);
+}
+// 16 packed bytes (32 codes in dim order) -> the 24-byte FP6 operand of those
+// 32 values: value i in bits [6 i, 6 i + 6) of six little-endian dwords
+__device__ __forceinline__ void e2m3_pack32(uint4 p, uint32_t (&o)[6]) {
   const uint32_t w[4] = {p.x, p.y, p.z, p.w};
-  uint32_t o[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t a = 0, b = 0;
+  for (int k = 0; k < 6; ++k) o[k] = 0;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {   // packed bytes 2k, 2k+1 of word i -> 4 output bytes each
-      const uint32_t b0 = (w[i] >> (16 * k)) & 0xFFu, b1 = (w[i] >> (16 * k + 8)) & 0xFFu;
-      const uint32_t v = e4m3_of_code(b0 & 15u) | (e4m3_of_code(b0 >> 4) << 8) | (e4m3_of_code(b1 & 15u) << 16) |
-                         (e4m3_of_code(b1 >> 4) << 24);
-      if (k == 0) a = v; else b = v;
-    }
-    o[2 * i] = a;
-    o[2 * i + 1] = b;
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t v = e2m3_of_code((w[i >> 3] >> (4 * (i & 7))) & 15u);
+    const int bit = 6 * i, k = bit >> 5, sh = bit & 31;
+    o[k] |= v << sh;
+    if (sh > 26) o[k + 1] |= v >> (32 - sh);
   }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // 16 packed bytes in the operand order of the V codes (for each 4-byte word: the
@@ -90,7 +91,8 @@ __device__ __forceinline__ void e4m3_expand32_split(uint4 p, uint4& lo, uint4& h
 }
 
 // Expands one (b, h, key block) into the LDS image the attention kernel copies:
-// the packed K codes of its 64 keys become E4M3 bytes in dim order, and the
+// the packed K codes of its 64 keys become FP6 E2M3 operands (each run of 32
+// dims in a 32-byte slot: 24 bytes of packed values, 8 unused), and the
 // operand-order V codes of its channels E4M3 bytes in the same operand order,
 // all at their permuted LDS offsets.
 template <int DP, int DV>
@@ -105,11 +107,11 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
   const uint8_t* kg = k_codes + (bh * kp.Lp + (long long)j * kBlock) * QROW;
   const uint8_t* vg = v_codes + u * VPK;
   for (int o = threadIdx.x * 16; o < KPK; o += 256 * 16) {
-    const int r = o / QROW, c = (o - r * QROW) / 8, x = kv_swz(DP, r);   // c: first of the two int8 pieces
-    uint4 lo, hi;
-    e4m3_expand32(*reinterpret_cast<const uint4*>(kg + o), lo, hi);
-    *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = lo;
-    *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = hi;
+    const int r = o / QROW, c = (o - r * QROW) / 8, x = kv_swz(DP, r);   // c: first of the slot's two pieces
+    uint32_t f6[6];
+    e2m3_pack32(*reinterpret_cast<const uint4*>(kg + o), f6);
+    *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+    *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
   }
   for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16) {
     const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);
@@ -119,6 +121,9 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
     *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = hi;
   }
 }
+
+// operand format code of FP6 E2M3 in v_mfma_*_f8f6f4 (cbsz / blgp)
+constexpr int kFp6 = 2;
 
 // s_waitcnt that waits until at most N vector-memory operations of this wave
 // are outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
@@ -248,17 +253,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   const bool mixed = work && a.route && a.head_kflag[bh] != 0;
   if (!__syncthreads_or(work)) return;
 
-  // Q codes of this lane's query (column) as E4M3: slice c, lane half hh holds
-  // dims [64 c + 32 hh, +32) (the K rows are read with the same split).
+  // Q codes of this lane's query (column) as FP6 E2M3: slice c, lane half hh
+  // holds dims [64 c + 32 hh, +32) (the K rows are read with the same split).
+  // The FP6 product uses the first six dwords of each operand.
   v8i qop[NC];
   float cq = 0.f;
   if (work) {
     const uint8_t* qrow = a.q_codes + ((long long)bh * Lp + wrow + col) * QROW;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      uint4 lo, hi;
-      e4m3_expand32(*reinterpret_cast<const uint4*>(qrow + 32 * c + 16 * hh), lo, hi);
-      qop[c] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      uint32_t f6[6];
+      e2m3_pack32(*reinterpret_cast<const uint4*>(qrow + 32 * c + 16 * hh), f6);
+      qop[c] = v8i{(int)f6[0], (int)f6[1], (int)f6[2], (int)f6[3], (int)f6[4], (int)f6[5], 0, 0};
     }
     cq = fmul_rn(a.q_scale[bh * NB + qblk], c0);
   }
@@ -322,14 +328,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     for (int v = 0; v < 16; ++v) { d0[v] = 0.f; d1[v] = 0.f; }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      // the 24 bytes of the slot: a full first piece and half of the second
       const v4i a0l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c]);
-      const v4i a0h = *reinterpret_cast<const v4i*>(Ks + koff[2 * c + 1]);
+      const v2i a0h = *reinterpret_cast<const v2i*>(Ks + koff[2 * c + 1]);
       const v4i a1l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c] + 32 * DP);
-      const v4i a1h = *reinterpret_cast<const v4i*>(Ks + koff[2 * c + 1] + 32 * DP);
-      const v8i a0 = v8i{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
-      const v8i a1 = v8i{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
-      d0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], d0, 0, 0, 0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[c], d1, 0, 0, 0, 0, 0, 0);
+      const v2i a1h = *reinterpret_cast<const v2i*>(Ks + koff[2 * c + 1] + 32 * DP);
+      const v8i a0 = v8i{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], 0, 0};
+      const v8i a1 = v8i{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], 0, 0};
+      d0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], d0, kFp6, kFp6, 0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[c], d1, kFp6, kFp6, 0, 0, 0, 0);
     }
   };
 

@@ -9,6 +9,7 @@ namespace rotattn {
 
 constexpr int kBlock = 64;   // tokens per quantization block and per flash key block
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
