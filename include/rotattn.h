@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ROTATTN_VERSION 2
+#define ROTATTN_VERSION 3
 
 /* error codes */
 #define ROTATTN_OK            0
@@ -165,9 +165,11 @@ int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_
  * non-NULL or block_err_tau is finite, qk->q_rope and qk->k_rope and v are
  * required (the FP16 path reads them); otherwise they may be NULL.
  * out: device fp16 with the problem's strides (may not alias inputs).
- * Workspace: ROTATTN_CALL_ATTENTION bytes: the int8 K/V block images the
- * INT4 kernel copies into LDS (about 2.5x the packed K + V codes), plus the
- * partial results of mixed rows when block_err_tau is finite.
+ * Workspace: ROTATTN_CALL_ATTENTION bytes: the K/V block images the INT4
+ * kernel copies into LDS (about 2.5x the packed K + V codes), the transposed
+ * fp16 V blocks of the FP16 path (L x D fp16 rounded up to whole blocks;
+ * written only when the FP16 path runs), plus the partial results of mixed
+ * rows when block_err_tau is finite.
  */
 int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                       const void* v, const uint8_t* head_fallback, void* out,
@@ -185,7 +187,8 @@ int rotattn_forward(const rotattn_problem* p, const rotattn_qk_buffers* qk, cons
 /*
  * Whole-call FP16 flash attention with 3D RoPE, no rotation or quantization:
  * the fallback for a whole denoising step (RotateAttention abstract).
- * Workspace: ROTATTN_CALL_FP16_FORWARD bytes (RoPE tables and RoPE'd copies).
+ * Workspace: ROTATTN_CALL_FP16_FORWARD bytes (RoPE tables, RoPE'd copies of
+ * Q and K, transposed V blocks).
  */
 int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k, const void* v, void* out,
                          void* workspace, size_t workspace_bytes, rotattn_stream_t stream);

@@ -9,52 +9,143 @@
 //
 // Same work layout as the INT4 kernel: S^T = K Q^T and O^T = V^T P^T with
 // v_mfma_f32_32x32x16_f16, one query column per lane, P rounded to fp16 in
-// registers as the B operand of the second product, O accumulated in fp32
-// by the matrix cores. Inputs are RoPE'd, unrotated Q/K (fp16, dense) and the
-// caller's fp16 V. The V tile is transposed into LDS in the key order of
-// the P operand so that each lane reads its operand with one 16-byte load.
+// registers as the B operand of the second product, O accumulated in fp32 by
+// the matrix cores and rescaled only when a row max of the wave grows. Inputs
+// are RoPE'd, unrotated Q/K (fp16, dense) and the caller's fp16 V. K rows go
+// straight from HBM into a two-stage LDS ring with direct-to-LDS loads (the
+// XOR permutation of their 16-byte pieces is applied to the source
+// addresses); V is staged the same way from a pre-pass that writes V^T per
+// (b, h, 64-key block) with its keys in the order of the P operand.
 #include "common.h"
+
+#include <cmath>
 
 namespace rotattn {
 
 __device__ __forceinline__ float exp2_hw16(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS stage of one key block: 64 K rows of D halves (16-byte pieces
+// XOR-permuted per row), then D rows of V^T, 64 halves each (permuted the same
+// way as 128-byte rows). 256 * D bytes; the pre-pass writes the V^T half.
 template <int D>
-__global__ __launch_bounds__(256) void fp16_attn_kernel(KProblem kp, AttnArgs a, int whole_call, float c0) {
-  constexpr int NC = D / 16;     // 16-deep slices per S tile (each lane half covers D/2 dims)
-  constexpr int NCT = D / 32;
-  constexpr int KP = D + 8;      // padded LDS row (halves)
-  constexpr int VP = kBlock + 8;
-  __shared__ __attribute__((aligned(16))) __half ks[kBlock * KP];
-  __shared__ __attribute__((aligned(16))) __half vt[D * VP];
+__host__ __device__ constexpr int f16_vt_bytes() { return 128 * D; }
+template <int D>
+__device__ __forceinline__ int f16_kswz(int r) { return D == 128 ? (r & 15) : kv_swz(128, r); }
+// key (within the block) whose value sits at position pos of a V^T row: the
+// order in which the P operand of the second product holds its keys
+__device__ __forceinline__ int f16_key_of_pos(int pos) {
+  return (pos & 32) + (pos & 16) + 8 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 1) + (pos & 3);
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int D>
+__global__ __launch_bounds__(256) void fp16_vt_kernel(KProblem kp, const __half* __restrict__ v, uint8_t* image) {
+  __shared__ __attribute__((aligned(16))) __half vt[kBlock][D + 8];
+  const long long u = blockIdx.x;
+  const long long bh = u / kp.NB;
+  const int j = (int)(u - bh * kp.NB);
+  const int b = (int)(bh / kp.H), h = (int)(bh - (long long)b * kp.H);
+  uint8_t* dst = image + u * f16_vt_bytes<D>();
+  for (int idx = threadIdx.x; idx < kBlock * D / 8; idx += 256) {
+    const int r = idx / (D / 8), pc = idx - r * (D / 8);
+    const int key = j * kBlock + r;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (key < kp.L)
+      val = *reinterpret_cast<const uint4*>(v + (long long)b * kp.sb + (long long)h * kp.sh +
+                                            (long long)key * kp.sl + pc * 8);
+    *reinterpret_cast<uint4*>(&vt[r][pc * 8]) = val;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < D * 8; idx += 256) {   // (channel, 8-position piece)
+    const int ch = idx >> 3, pc = idx & 7;
+    __half hv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = vt[f16_key_of_pos(8 * pc + e)][ch];
+    *reinterpret_cast<uint4*>(dst + ch * 128 + 16 * (pc ^ kv_swz(128, ch))) = *reinterpret_cast<const uint4*>(hv);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs a, int whole_call, float c0) {
+  constexpr int NC = D / 16;       // 16-deep slices of the head dim
+  constexpr int NCT = D / 32;      // 32-channel output tiles
+  constexpr int KROWB = 2 * D, VT0 = 64 * KROWB, VTB = f16_vt_bytes<D>();
+  constexpr int IMG = VT0 + VTB;
+  constexpr int NDK = VT0 / 4096, NDV = VTB / 4096;   // 16-byte copies per thread per stage
+  static_assert(VT0 % 4096 == 0 && VTB % 4096 == 0, "a stage must split evenly over the workgroup");
+  // one LDS array per stage, indexed by compile-time stage numbers
+  __shared__ __attribute__((aligned(16))) uint8_t stg0[IMG];
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[IMG];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
   const int L = kp.L, Lp = kp.Lp, NB = kp.NB;
   const int b = blockIdx.z, h = blockIdx.y, bh = b * kp.H + h;
   const int wrow = blockIdx.x * 128 + 32 * wave;
   const bool active = wrow < L;
   const int qblk = wrow / kBlock;
+  // per wave: `full` rows take every key block on this path, `mixed` rows the
+  // flagged key blocks only (their other blocks ran on the INT4 path)
   bool full = false, mixed = false;
   if (active) {
-    full = whole_call || (a.head_mask != nullptr && a.head_mask[bh] != 0) ||
-           (a.route && a.q_flag[bh * NB + qblk] != 0);
+    full = whole_call || (a.head_mask != nullptr && uniform_byte(a.head_mask, bh) != 0) ||
+           (a.route && uniform_byte(a.q_flag, bh * NB + qblk) != 0);
     mixed = !full && a.route && a.head_kflag[bh] != 0;
   }
-  const bool any_full = __syncthreads_or(full);
-  const bool any_mixed = __syncthreads_or(mixed);
+  const bool any_full = __builtin_amdgcn_readfirstlane(__syncthreads_or(full)) != 0;
+  const bool any_mixed = __builtin_amdgcn_readfirstlane(__syncthreads_or(mixed)) != 0;
   if (!any_full && !any_mixed) return;
 
   const int row = wrow + col;
   v8h qop[NC];
   if (full || mixed) {
-    const __half* qrow = a.q_rope + ((long long)bh * L + (row < L ? row : L - 1)) * D + hh * (D / 2);
+    const __half* qrow = a.q_rope + ((long long)bh * L + (row < L ? row : L - 1)) * D + 8 * hh;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint4 u = reinterpret_cast<const uint4*>(qrow)[c];
+      const uint4 u = *reinterpret_cast<const uint4*>(qrow + 16 * c);
       qop[c] = *reinterpret_cast<const v8h*>(&u);
     }
   }
+  // LDS offsets: K row col (and col + 32) at piece 2c + hh (dims [16c + 8hh, +8));
+  // V^T row ct*32 + col at piece 4s + 2u + hh
+  int koff[NC], voff[4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = col * KROWB + 16 * ((2 * c + hh) ^ f16_kswz<D>(col));
+#pragma unroll
+  for (int su = 0; su < 4; ++su) voff[su] = VT0 + col * 128 + 16 * ((2 * su + hh) ^ kv_swz(128, col));
+
+  const uint8_t* kflag = a.route ? a.k_flag + (long long)bh * NB : nullptr;
+  // key blocks this workgroup visits: all when some row runs whole on this
+  // path, else the flagged ones only (wave-uniform)
+  auto next_block = [&](int j) __attribute__((always_inline)) {
+    if (!any_full && kflag != nullptr)
+      while (j < NB && uniform_byte(kflag, j) == 0) ++j;
+    return __builtin_amdgcn_readfirstlane(j);
+  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // thread tid fills LDS bytes [i * 4096 + 16 * tid, +16) of each stage; for the
+  // K half that is row kr[i], physical piece kp_[i], holding logical piece
+  // kp_[i] ^ swz(row) of key j * 64 + kr[i] (the last key row stands in past L:
+  // those keys are masked out of S)
+  const __half* kbase = a.k_rope + (long long)bh * L * D;
+  const uint8_t* vimg = a.f16_vt + (long long)bh * NB * VTB + tid * 16;
+  int krow[NDK], kpiece[NDK];
+#pragma unroll
+  for (int i = 0; i < NDK; ++i) {
+    const int o = i * 4096 + tid * 16;
+    krow[i] = o / KROWB;
+    kpiece[i] = ((o % KROWB) >> 4) ^ f16_kswz<D>(krow[i]);
+  }
+  auto dma_block = [&](int j, uint8_t* stage_base) __attribute__((always_inline)) {
+    const uint32_t dst = lds_addr(stage_base) + wave_u * 1024;
+#pragma unroll
+    for (int i = 0; i < NDK; ++i) {
+      const int key = min(j * kBlock + krow[i], L - 1);
+      lds_copy16(kbase + (long long)key * D + 8 * kpiece[i], dst + i * 4096);
+    }
+    const uint8_t* vsrc = vimg + (long long)j * VTB;
+#pragma unroll
+    for (int i = 0; i < NDV; ++i) lds_copy16(vsrc + i * 4096, dst + VT0 + i * 4096);
+  };
 
   float m_run = -INFINITY, l_part = 0.f;
   v16f o_acc[NCT];
@@ -63,44 +154,15 @@ __global__ __launch_bounds__(256) void fp16_attn_kernel(KProblem kp, AttnArgs a,
 #pragma unroll
     for (int v = 0; v < 16; ++v) o_acc[ct][v] = 0.f;
 
-  for (int j = 0; j < NB; ++j) {
-    const bool kflag = a.route && a.k_flag[bh * NB + j] != 0;
-    if (!any_full && !kflag) continue;
-    __syncthreads();
-    // K tile: 64 keys x D halves, rows at or beyond L are zero.
-    for (int idx = threadIdx.x; idx < kBlock * D / 8; idx += 256) {
-      const int r = idx / (D / 8), c8 = idx - r * (D / 8);
-      const int key = j * kBlock + r;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (key < L) u = *reinterpret_cast<const uint4*>(a.k_rope + ((long long)bh * L + key) * D + c8 * 8);
-      *reinterpret_cast<uint4*>(&ks[r * KP + c8 * 8]) = u;
-    }
-    // V tile, transposed: vt[channel][pos] with pos the operand order of key r.
-    for (int idx = threadIdx.x; idx < kBlock * D / 8; idx += 256) {
-      const int r = idx / (D / 8), c8 = idx - r * (D / 8);
-      const int key = j * kBlock + r;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (key < L)
-        u = *reinterpret_cast<const uint4*>(a.v + (long long)b * kp.sb + (long long)h * kp.sh +
-                                            (long long)key * kp.sl + c8 * 8);
-      const __half* hv = reinterpret_cast<const __half*>(&u);
-      const int s = r >> 5, rr = r & 31;
-      const int pos = 32 * s + 16 * (rr >> 4) + 8 * ((rr >> 2) & 1) + 4 * ((rr >> 3) & 1) + (rr & 3);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(c8 * 8 + e) * VP + pos] = hv[e];
-    }
-    __syncthreads();
-    if (!(full || (mixed && kflag))) continue;
-
+  auto compute = [&](const uint8_t* Ks, int j) __attribute__((always_inline)) {
     v16f sacc[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[s][v] = 0.f;
-      const __half* krow = ks + (32 * s + col) * KP + hh * (D / 2);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const v8h kop = *reinterpret_cast<const v8h*>(krow + 8 * c);
+        const v8h kop = *reinterpret_cast<const v8h*>(Ks + koff[c] + s * 32 * KROWB);
         sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[c], sacc[s], 0, 0, 0);
       }
     }
@@ -116,31 +178,59 @@ __global__ __launch_bounds__(256) void fp16_attn_kernel(KProblem kp, AttnArgs a,
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_hw16(m_run - m_new);
+    if (__ballot(m_new > m_run) != 0ull) {   // rescale only when some row max grew
+      const float alpha = exp2_hw16(m_run - m_new);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o_acc[ct][v] *= alpha;
+      l_part *= alpha;
+      m_run = m_new;
+    }
     v8h pop[2][2];
     float psum = 0.f;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float P = exp2_hw16(sacc[s][v] - m_new);
+        const float P = exp2_hw16(sacc[s][v] - m_run);
         psum += P;
         pop[s][v >> 3][v & 7] = (_Float16)P;
       }
-    l_part = alpha * l_part + psum;
+    l_part += psum;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o_acc[ct][v] *= alpha;
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const v8h vop = *reinterpret_cast<const v8h*>(&vt[(ct * 32 + col) * VP + 32 * s + 16 * u + 8 * hh]);
+          const v8h vop = *reinterpret_cast<const v8h*>(Ks + voff[2 * s + u] + ct * 32 * 128);
           o_acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[s][u], o_acc[ct], 0, 0, 0);
         }
-    }
-    m_run = m_new;
+  };
+
+  // two-stage ring: entering the iteration for block j, j is in LDS; the
+  // iteration starts the copy of the next block into the other stage, computes
+  // j, waits for the copy and ends with one barrier
+  int j = next_block(0);
+  if (j < NB) dma_block(j, stg0);
+  wait_vmcnt<0>();
+  stage_barrier();
+  auto iter = [&](auto s_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_tag)::value;
+    uint8_t* cur = S == 0 ? stg0 : stg1;
+    uint8_t* oth = S == 0 ? stg1 : stg0;
+    const int jn = (j + 1 < NB) ? next_block(j + 1) : NB;
+    if (jn < NB) dma_block(jn, oth);
+    if (full || (mixed && uniform_byte(kflag, j) != 0)) compute(cur, j);
+    wait_vmcnt<0>();
+    stage_barrier();
+    j = jn;
+  };
+  while (j < NB) {
+    iter(std::integral_constant<int, 0>());
+    if (j >= NB) break;
+    iter(std::integral_constant<int, 1>());
   }
 
   if (!(full || mixed)) return;
@@ -168,19 +258,33 @@ __global__ __launch_bounds__(256) void fp16_attn_kernel(KProblem kp, AttnArgs a,
     const float a2 = (m_run == -INFINITY) ? 0.f : exp2_hw16(m_run - mm);
     const float inv = 1.0f / (a1 * l1 + a2 * l);
     const float* po = a.part_o + ((long long)bh * Lp + row) * D;
+    float4 p1[NCT][4];   // all loads first: the stores below may alias them for the compiler
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) p1[ct][g] = *reinterpret_cast<const float4*>(po + ct * 32 + 8 * g + 4 * hh);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int ch = ct * 32 + 8 * g + 4 * hh;
-        const float4 p1 = *reinterpret_cast<const float4*>(po + ch);
-        const float o1[4] = {p1.x, p1.y, p1.z, p1.w};
+        const float o1[4] = {p1[ct][g].x, p1[ct][g].y, p1[ct][g].z, p1[ct][g].w};
         __half hv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn((a1 * o1[e] + a2 * o_acc[ct][4 * g + e]) * inv);
-        *reinterpret_cast<uint2*>(orow + ch) = *reinterpret_cast<const uint2*>(hv);
+        *reinterpret_cast<uint2*>(orow + ct * 32 + 8 * g + 4 * hh) = *reinterpret_cast<const uint2*>(hv);
       }
   }
+}
+
+hipError_t launch_fp16_vt(const KProblem& kp, const __half* v, uint8_t* image, hipStream_t s) {
+  const unsigned units = (unsigned)((long long)kp.B * kp.H * kp.NB);
+  if (kp.D == 128)
+    hipLaunchKernelGGL((fp16_vt_kernel<128>), dim3(units), dim3(256), 0, s, kp, v, image);
+  else if (kp.D == 64)
+    hipLaunchKernelGGL((fp16_vt_kernel<64>), dim3(units), dim3(256), 0, s, kp, v, image);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, bool whole_call, hipStream_t s) {

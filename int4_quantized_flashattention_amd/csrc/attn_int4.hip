@@ -125,50 +125,6 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
 // operand format code of FP6 E2M3 in v_mfma_*_f8f6f4 (cbsz / blgp)
 constexpr int kFp6 = 2;
 
-// s_waitcnt that waits until at most N vector-memory operations of this wave
-// are outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-  asm volatile("" ::: "memory");
-}
-// Direct-to-LDS copies: lane l's 16 (or 4) bytes at `src` land at LDS byte
-// address m0 + 16 l (or 4 l). Written as inline asm rather than the builtin so
-// that the compiler does not make LDS reads wait for them: once the stage loop
-// wraps around it can no longer tell which stage a builtin copy writes and
-// waits for every copy in flight. The callers order copies and reads with
-// explicit vmcnt waits and barriers. No register output: the copy writes LDS
-// only, and its address registers are read when it issues. M0 is restored.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t m0) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(src)
-      : "memory");
-}
-__device__ __forceinline__ void lds_copy4(const void* src, uint32_t m0) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(src)
-      : "memory");
-}
-
-// Workgroup barrier without a memory fence: LDS stages are filled by
-// direct-to-LDS loads whose completion the caller has already waited for.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
 // 64: the packed K and V codes (prefetched into registers during the previous
 // block) are unpacked once into one of two LDS stages, one barrier, then every
@@ -274,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   // result is wave-uniform, which keeps the loop control in scalar registers
   auto next_block = [&](int j) __attribute__((always_inline)) {
     if (kflag != nullptr)
-      while (j < NB && kflag[j] != 0) ++j;   // FP16 tile: the other path takes it
+      while (j < NB && uniform_byte(kflag, j) != 0) ++j;   // FP16 tile: the other path takes it
     return __builtin_amdgcn_readfirstlane(j);
   };
   // Block j's image goes to LDS stage `stage` with NDMA direct-to-LDS loads per

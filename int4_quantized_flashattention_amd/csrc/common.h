@@ -65,6 +65,66 @@ __host__ __device__ constexpr int kv_swz(int row_bytes, int r) {
   return row_bytes == 128 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
+// s_waitcnt that waits until at most N vector-memory operations of this wave
+// are outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+// Direct-to-LDS copies: lane l's 16 (or 4) bytes at `src` land at LDS byte
+// address m0 + 16 l (or 4 l). Written as inline asm rather than the builtin so
+// that the compiler does not make LDS reads wait for them: once the stage loop
+// wraps around it can no longer tell which stage a builtin copy writes and
+// waits for every copy in flight. The callers order copies and reads with
+// explicit vmcnt waits and barriers. No register output: the copy writes LDS
+// only, and its address registers are read when it issues. M0 is restored.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void* src, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+
+// Workgroup barrier without a memory fence: LDS stages are filled by
+// direct-to-LDS loads whose completion the caller has already waited for.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Byte i of a byte array that no thread writes during the kernel, for a
+// wave-uniform base and i, read through the scalar unit: the dword-aligned
+// word holding the byte is loaded (it stays inside the 4-byte granule of a
+// valid byte) and the byte shifted out. The address goes through
+// readfirstlane so that the load is scalar even where the compiler cannot
+// prove it uniform. A vector load here would share the vmcnt counter with the
+// direct-to-LDS copies in flight and wait for all of them.
+__device__ __forceinline__ uint32_t uniform_byte(const uint8_t* base, int i) {
+  const uint64_t addr = reinterpret_cast<uintptr_t>(base) + (uint64_t)(int64_t)i;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
+  const uint32_t w = *reinterpret_cast<const_u32p>(((uint64_t)hi << 32) | (lo & ~3u));
+  return (w >> (8 * (lo & 3u))) & 0xFFu;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
@@ -96,6 +156,7 @@ struct AttnArgs {
   const uint8_t* head_mask;     // [B*H] or null
   const uint8_t* v_codes; const float* v_scale;
   const uint8_t* kv_image;      // [B*H][NB] LDS images of the K/V blocks (kv_image_bytes each)
+  const uint8_t* f16_vt;        // [B*H][NB] V^T blocks of the FP16 path (128 * D bytes each)
   const __half* q_rope; const __half* k_rope; const __half* v;   // FP16 path inputs
   __half* out;
   float* part_o; float* part_m; float* part_l;   // INT4 partials of mixed rows [B][H][Lp][D], [B][H][Lp]
@@ -112,5 +173,6 @@ hipError_t launch_rope_copy(const KProblem& kp, const __half* x, const float* ta
 hipError_t launch_vquant(const KProblem& kp, const __half* v, uint32_t* absmax_bits, const VOut& o, hipStream_t s);
 hipError_t launch_kv_image(const KProblem& kp, const AttnArgs& a, uint8_t* image, hipStream_t s);
 hipError_t launch_int4_attention(const KProblem& kp, const AttnArgs& a, bool dump, hipStream_t s);
+hipError_t launch_fp16_vt(const KProblem& kp, const __half* v, uint8_t* image, hipStream_t s);
 hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, bool whole_call, hipStream_t s);
 }  // namespace rotattn

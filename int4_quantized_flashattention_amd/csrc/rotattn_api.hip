@@ -75,7 +75,7 @@ int derive(const rotattn_problem* p, Derived* d) {
 
 // Workspace carve-up of every call. Offsets are 256-byte aligned.
 struct Layout {
-  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0, img = 0;
+  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0, img = 0, vt = 0;
   size_t total = 0;
 };
 
@@ -95,6 +95,7 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
   const size_t pm_b = (size_t)BH * d.Lp * sizeof(float);
   const size_t rope_b = (size_t)BH * p->L * p->D * 2;
   const size_t img_b = (size_t)BH * d.NB * kv_image_bytes((int)d.Dp, p->D);
+  const size_t vt_b = (size_t)BH * d.NB * 128 * p->D;
   switch (call) {
     case ROTATTN_CALL_QUANTIZE_QK:
       L.tab = take(tab_bytes);
@@ -104,16 +105,18 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
       break;
     case ROTATTN_CALL_ATTENTION:
       L.img = take(img_b);
+      L.vt = take(vt_b);
       if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
       break;
     case ROTATTN_CALL_FORWARD:
       L.vcodes = take(vcodes_b); L.vscale = take(vscale_b); L.vcolsum = take(vcolsum_b);
       L.absmax = take(absmax_b);
       L.img = take(img_b);
+      L.vt = take(vt_b);
       if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
       break;
     case ROTATTN_CALL_FP16_FORWARD:
-      L.tab = take(tab_bytes); L.qr = take(rope_b); L.kr = take(rope_b);
+      L.tab = take(tab_bytes); L.qr = take(rope_b); L.kr = take(rope_b); L.vt = take(vt_b);
       break;
     case ROTATTN_CALL_DEBUG_DUMP:
       L.img = take(img_b);
@@ -178,9 +181,11 @@ int attention_impl(const rotattn_problem* p, const Derived& d, const rotattn_qk_
   int rc = launched(launch_kv_image(d.kp, a, img, s));
   if (rc != ROTATTN_OK) return rc;
   rc = launched(launch_int4_attention(d.kp, a, false, s));
-  if (rc != ROTATTN_OK) return rc;
-  if (fp16_needed) rc = launched(launch_fp16_attention(d.kp, a, false, s));
-  return rc;
+  if (rc != ROTATTN_OK || !fp16_needed) return rc;
+  uint8_t* vt = at<uint8_t>(ws, L.vt);
+  a.f16_vt = vt;
+  if ((rc = launched(launch_fp16_vt(d.kp, a.v, vt, s))) != ROTATTN_OK) return rc;
+  return launched(launch_fp16_attention(d.kp, a, false, s));
 }
 
 int check_attention_args(const rotattn_problem* p, const rotattn_qk_buffers* qk, const void* v,
@@ -347,6 +352,9 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
   a.v = static_cast<const __half*>(v);
   a.out = static_cast<__half*>(out);
   a.route = false;
+  uint8_t* vt = at<uint8_t>(workspace, L.vt);
+  a.f16_vt = vt;
+  if ((rc = launched(launch_fp16_vt(d.kp, a.v, vt, s))) != ROTATTN_OK) return rc;
   return launched(launch_fp16_attention(d.kp, a, true, s));
 }
 

@@ -37,7 +37,7 @@ def test_exports_match_header():
 
 def test_version_and_strerror():
     lib = _lib()
-    assert lib.rotattn_version() == 2
+    assert lib.rotattn_version() == 3
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.rotattn_strerror(code)
 
@@ -66,12 +66,13 @@ def test_sizes_720p():
     # the attention workspace holds one 16384-byte int8 LDS image per (head, key block): 64 K rows of
     # 128 bytes and 128 V rows of 64 bytes
     img = 40 * 1182 * 16384
-    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img
+    vt = 40 * 1182 * 64 * 128 * 2   # transposed fp16 V blocks of the FP16 path
+    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img + vt
     assert Bd.workspace_bytes(p, Bd.CALL_DEBUG_DUMP) == img
     # partial buffers on top only when block routing is on
     pm = Bd.problem_from_workload(W.WORKLOADS["mixed"])
     img_m = 12 * 512 * 20480   # D' = 192: 64 x 192 + 128 x 64
-    assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) >= img_m + 12 * 32768 * 128 * 4
+    assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) >= img_m + 12 * 512 * 64 * 128 * 2 + 12 * 32768 * 128 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
