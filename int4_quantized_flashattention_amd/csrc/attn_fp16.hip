@@ -166,18 +166,31 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
         sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[c], sacc[s], 0, 0, 0);
       }
     }
-    const int key0 = j * kBlock;
-    float mx = -INFINITY;
+    // row max of the raw scores (c0 > 0, so max(S c0) = max(S) c0); keys
+    // past L only in the last block
+    float mx;
+    if (j * kBlock + kBlock > L) {
+      const int key0 = j * kBlock;
+      mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
-        sacc[s][v] = (key < L) ? sacc[s][v] * c0 : -INFINITY;
-        mx = fmaxf(mx, sacc[s][v]);
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key >= L) sacc[s][v] = -INFINITY;
+          mx = fmaxf(mx, sacc[s][v]);
+        }
+    } else {
+      float ma = fmaxf(sacc[0][0], sacc[1][0]), mb = fmaxf(sacc[0][1], sacc[1][1]);
+#pragma unroll
+      for (int v = 2; v < 16; v += 2) {
+        ma = fmaxf(fmaxf(ma, sacc[0][v]), sacc[1][v]);
+        mb = fmaxf(fmaxf(mb, sacc[0][v + 1]), sacc[1][v + 1]);
       }
+      mx = fmaxf(ma, mb);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * c0);
     if (__ballot(m_new > m_run) != 0ull) {   // rescale only when some row max grew
       const float alpha = exp2_hw16(m_run - m_new);
 #pragma unroll
@@ -187,17 +200,29 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
       l_part *= alpha;
       m_run = m_new;
     }
+    // P = 2^(S c0 - m): exponents first, then the exp2s, as independent streams
+    const float nm = -m_run;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[s][v] = fmaf(sacc[s][v], c0, nm);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[s][v] = exp2_hw16(sacc[s][v]);
+    __builtin_amdgcn_sched_barrier(0);
     v8h pop[2][2];
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float P = exp2_hw16(sacc[s][v] - m_run);
-        psum += P;
-        pop[s][v >> 3][v & 7] = (_Float16)P;
+        ps[v & 3] += sacc[s][v];
+        pop[s][v >> 3][v & 7] = (_Float16)sacc[s][v];
       }
-    l_part += psum;
+    l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -222,7 +247,10 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
     uint8_t* oth = S == 0 ? stg1 : stg0;
     const int jn = (j + 1 < NB) ? next_block(j + 1) : NB;
     if (jn < NB) dma_block(jn, oth);
-    if (full || (mixed && uniform_byte(kflag, j) != 0)) compute(cur, j);
+    if (full || (mixed && uniform_byte(kflag, j) != 0)) {
+      compute(cur, j);
+      __builtin_amdgcn_s_setprio(0);
+    }
     wait_vmcnt<0>();
     stage_barrier();
     j = jn;

@@ -126,13 +126,13 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
 constexpr int kFp6 = 2;
 
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
-// 64: the packed K and V codes (prefetched into registers during the previous
-// block) are unpacked once into one of two LDS stages, one barrier, then every
-// wave runs two S^T tiles, the online softmax and four O^T tiles on the
-// matrix cores. O is accumulated in int32 by the matrix cores and folded into
-// the float32 accumulator only when some row max of the wave grows (the
-// rescale factor is exactly 1 otherwise).
-template <int DP, int DV, int NW, int NST, int OCC, bool EARLY, bool DUMP>
+// 64, the block's LDS image (FP6 K rows, E4M3 V^T rows, the K scale) arrives in
+// one stage of an NST-stage ring through direct-to-LDS loads issued NST - 1
+// blocks ahead; one barrier per block. Every wave computes S^T of its 32
+// queries (FP6 products), the online softmax and P codes in registers, and
+// O^T on the FP8 matrix cores into a float32 accumulator kept at the running
+// max, rescaled only when some row max of the wave grows.
+template <int DP, int DV, int NW, int NST, int OCC, bool DUMP>
 __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
   constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP8 product each)
@@ -276,9 +276,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   for (int s = 0; s < 2; ++s) voff[s] = col * 64 + 16 * ((2 * hh + s) ^ kv_swz(64, col));
 
   // S^T of the block in `stage` (the integer q.k as exact floats), as two
-  // 32-key halves, on the FP8 matrix cores (E4M3 codes, no block scaling)
+  // 32-key halves, on the FP6 matrix path (E2M3 codes, no block scaling)
   v16f s0, s1;   // S^T of the block in the softmax
-  v16f n0, n1;   // S^T of the next block, on the matrix cores meanwhile
   auto qk = [&](const uint8_t* Ks, v16f& d0, v16f& d1) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) { d0[v] = 0.f; d1[v] = 0.f; }
@@ -348,6 +347,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     const float nm15 = -fsub_rn(m_run, log2_15);
     v4i pop[2];
     float ls0 = 0.f, ls1 = 0.f;
+    if constexpr (!kRagged && !DUMP) {
+      // full block: every exponent first (in place, S^T is not needed after
+      // this), then every exp2, so that the two run as independent streams
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { s0[v] = fmaf(s0[v], cs, nm15); s1[v] = fmaf(s1[v], cs, nm15); }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { s0[v] = exp2_hw(s0[v]); s1[v] = exp2_hw(s1[v]); }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -356,12 +365,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int v = 4 * kq + bb;
-          float t = fmaf(s == 0 ? s0[v] : s1[v], cs, nm15);
-          if (kRagged) {
-            const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
-            if (key >= L) t = -INFINITY;
+          if constexpr (!kRagged && !DUMP) {
+            p15[bb] = s == 0 ? s0[v] : s1[v];
+          } else {
+            float t = fmaf(s == 0 ? s0[v] : s1[v], cs, nm15);
+            if (kRagged) {
+              const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
+              if (key >= L) t = -INFINITY;
+            }
+            p15[bb] = exp2_hw(t);
           }
-          p15[bb] = exp2_hw(t);
           if (bb & 1) ls1 += p15[bb]; else ls0 += p15[bb];
         }
         // both halves of w are written below, so its initial value does not
@@ -386,6 +399,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     l15 += ls0 + ls1;
     // O^T += V^T (pq + 8)^T: the zero-point correction rides inside the product
     const v8i pb = v8i{pop[0][0], pop[0][1], pop[0][2], pop[0][3], pop[1][0], pop[1][1], pop[1][2], pop[1][3]};
+    // raised wave priority while this wave issues its matrix products (P.V
+    // here, S^T of the next block after it), so the matrix cores are fed
+    // promptly while the other waves of the SIMD run their softmax
+    if constexpr (!kRagged) __builtin_amdgcn_s_setprio(1);
     const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -446,18 +463,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     const bool issued = q[NST - 1] < NB;
     if (issued) dma_block(q[NST - 1], SL());
     if (work) {
-      // S^T of the next block (stale data when there is no next block:
-      // computed, never used). EARLY issues it before this block's softmax,
-      // into a second register set, so the matrix cores work on it meanwhile.
-      if constexpr (EARLY) {
-        qk(stage(S1()), n0, n1);
-        softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
-        s0 = n0;
-        s1 = n1;
-      } else {
-        softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
-        qk(stage(S1()), s0, s1);
-      }
+      // S^T of the next block after this block's P.V (stale data when there
+      // is no next block: computed, never used)
+      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
+      qk(stage(S1()), s0, s1);
+      __builtin_amdgcn_s_setprio(0);
     }
     // q[2] must have landed before the next iteration reads it
     if (DUMP || NST == 3 || !issued) wait_vmcnt<0>();
@@ -543,9 +553,6 @@ struct Shape {
   static constexpr int kWaves = 4;
   static constexpr int kOcc = (DP == 128) ? 3 : 2;
   static constexpr int kStages = (kOcc * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3;
-  // next block's S^T issued before the softmax (32 more registers per lane);
-  // slower than the occupancy it costs at every shape measured
-  static constexpr bool kEarly = false;
 };
 
 template <int DP, int DV>
@@ -553,14 +560,13 @@ static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump
                                 hipStream_t s) {
   using S = Shape<DP, DV>;
   constexpr int W = S::kWaves, NS = S::kStages, OC = S::kOcc;
-  constexpr bool E = S::kEarly;
   if (dump) {
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, E, true>), dim3(a.n_units), dim3(W * 64), 0, s, kp, a,
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true>), dim3(a.n_units), dim3(W * 64), 0, s, kp, a,
                        c0, l15);
   } else {
     const int ntiles = (kp.L + 32 * W - 1) / (32 * W);
     dim3 grid(ntiles * kp.H * kp.B);
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, E, false>), grid, dim3(W * 64), 0, s, kp, a, c0, l15);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false>), grid, dim3(W * 64), 0, s, kp, a, c0, l15);
   }
   return hipGetLastError();
 }
