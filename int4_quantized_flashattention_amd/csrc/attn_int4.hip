@@ -197,6 +197,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     h = bhl - b * kp.H;
     row_base = (logical - bhl * ntiles) * (32 * NW);
   }
+  // workgroup-uniform: keep them (and every pointer derived from them) in
+  // scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  row_base = __builtin_amdgcn_readfirstlane(row_base);
   const int bh = b * kp.H + h;
   const int wrow = row_base + 32 * wave;
   const bool active = (wrow < L) && (!DUMP || wave < 2);
