@@ -26,6 +26,10 @@ What it computes, step by step, in the pages' order:
      (RotateAttention abstract), using the block mask of RainFusion2.0
      section 3.1 (a tile is skipped by one path and computed by the other),
      and a log-sum-exp merge of the two partial results.
+  6. Block-sparse attention (RainFusion2.0 sections 3.1, 3.2, 3.4): block
+     means as representative tokens, top-n key blocks per query block by
+     the score of the means, the first-frame sink on top, and the INT4 loop
+     over the kept key blocks only.
 
 Floating point: every step that decides an integer (a Q/K/V code, a block
 flag, a P code) is evaluated in float32 with the operation order stated in each
@@ -463,6 +467,100 @@ def merge(O1, m1, l1, O2, m2, l2):
     a1 = np.where(np.isneginf(m1), 0.0, np.exp2(m1 - m))
     a2 = np.where(np.isneginf(m2), 0.0, np.exp2(m2 - m))
     return (a1[:, None] * O1 + a2[:, None] * O2) / (a1 * l1 + a2 * l2)[:, None]
+
+
+# --------------------------------------------------------------------------
+# 6. block-sparse mask (RainFusion2.0, sections 3.1, 3.2 and 3.4)
+# --------------------------------------------------------------------------
+
+def sink_end(L: int, prefix: int, grid) -> int:
+    """Tokens [0, sink_end) take part in full attention: the text prefix and the first video frame.
+
+    RainFusion2.0 section 3.4 "First Frame Sink": the queries of the first
+    frame attend to every key and every query attends to the keys of the
+    first frame; the first-frame tokens are grouped with the text tokens so
+    that both take part in full attention. Reading: in the token order used
+    here (text prefix, then frames 0, 1, ... in [F, H, W] order) that set is
+    the prefix followed by the grid_h * grid_w tokens of frame 0.
+    """
+    T, Hh, W = grid
+    return min(L, prefix + (Hh * W if T > 0 else 0))
+
+
+def block_means(x16, prefix, grid, split, base) -> np.ndarray:
+    """Representative token of every 64-token block (RainFusion2.0 section 3.2).
+
+    The block mean of the RoPE'd rows (RoPE in float32 as in apply_rope),
+    averaged in float64 over the block's valid tokens (a ragged last block
+    averages only its tokens below L). Reading: the means are taken on the
+    RoPE'd Q and K, the vectors whose products the attention scores are;
+    the Hadamard rotation would not change any score (it is orthonormal).
+    Returns float64 [NB, D].
+    """
+    xr = apply_rope(x16.astype(F32), prefix, grid, split, base)
+    L, D = xr.shape
+    nb = n_blocks(L)
+    out = np.zeros((nb, D), dtype=F64)
+    for i in range(nb):
+        out[i] = xr[i * BLOCK:min(L, (i + 1) * BLOCK)].astype(F64).mean(axis=0)
+    return out
+
+
+def block_scores(q_means, k_means) -> np.ndarray:
+    """S_hat[i, j] = q_hat_i . k_hat_j (RainFusion2.0 section 3.2), float64 [NBq, NBk].
+
+    No 1/sqrt(d) factor: S_hat only ranks the key blocks of each query block.
+    """
+    return np.asarray(q_means, dtype=F64) @ np.asarray(k_means, dtype=F64).T
+
+
+def sparse_block_mask(s_hat, topn: int, L: int, prefix: int, grid) -> np.ndarray:
+    """Block mask M [NB, NB] of the block-sparse flash loop (RainFusion2.0 sections 3.1, 3.2, 3.4).
+
+    M[i, j] = 1 for the topn key blocks j with the largest S_hat[i, j]
+    (reading of "the top-n important blocks K_j for each block Q_i"; the
+    page's "TopN(S_hat, dim=0)" is read as per query block; equal scores are
+    taken in ascending j), then the first-frame sink on top: every key block
+    that holds a sink token is kept for every query block, and every query
+    block that holds a sink token keeps every key block.
+    """
+    s_hat = np.asarray(s_hat, dtype=F64)
+    nb = s_hat.shape[0]
+    M = np.zeros((nb, nb), dtype=bool)
+    n = min(int(topn), nb)
+    for i in range(nb):
+        order = sorted(range(nb), key=lambda j: (-s_hat[i, j], j))
+        M[i, order[:n]] = True
+    ns = -(-sink_end(L, prefix, grid) // BLOCK)     # blocks holding a sink token
+    M[:, :ns] = True
+    M[:ns, :] = True
+    return M
+
+
+def sparse_forward_head(q16, k16, v16, *, prefix, grid, split, base, rotation, topn, block_mask=None,
+                        rows=None):
+    """Block-sparse INT4 attention of one head (RainFusion2.0 section 3.1: Q_i K_j^T and P_ij V_j
+    are skipped where M[i, j] = 0), with the quantized loop of int4_flash_rows.
+
+    block_mask: bool [NB, NB] to use instead of the one computed from the
+    block means (the GPU tests pass the mask the GPU chose after checking it
+    against s_hat). Returns dict(out, rows, mask, s_hat, q, k, v codes).
+    """
+    L, D = q16.shape
+    qp = qk_prologue(q16, prefix, grid, split, base, rotation)
+    kp = qk_prologue(k16, prefix, grid, split, base, rotation)
+    vc, sv, colsum = quantize_v(v16)
+    s_hat = block_scores(block_means(q16, prefix, grid, split, base), block_means(k16, prefix, grid, split, base))
+    M = sparse_block_mask(s_hat, topn, L, prefix, grid) if block_mask is None else np.asarray(block_mask, bool)
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, D), dtype=F64)
+    for qb in np.unique(rows // BLOCK):
+        sel = (rows // BLOCK) == qb
+        p1 = int4_flash_rows(qp["codes"], qp["scale"], kp["codes"], kp["scale"], vc, sv, colsum,
+                             L, D, rows[sel], key_blocks=M[qb])
+        out[sel] = p1["O_scaled"] / p1["l"][:, None]
+    return {"out": out, "rows": rows, "mask": M, "s_hat": s_hat, "q": qp, "k": kp, "v_codes": vc,
+            "v_scale": sv, "v_colsum": colsum}
 
 
 # --------------------------------------------------------------------------

@@ -574,3 +574,136 @@ def test_exact_attention_brute():
     got = O.exact_attention(q, k, v, prefix=prefix, grid=grid, split=split, base=10000.0)
     want = BF.softmax_attention_brute(rope(q), rope(k), v, 1 / math.sqrt(D))
     assert np.allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# block-sparse mask (RainFusion2.0 sections 3.1, 3.2, 3.4)
+# --------------------------------------------------------------------------
+
+def test_sink_end_closed_forms():
+    """The sink is the text prefix plus the grid_h * grid_w tokens of frame 0 (clamped to L)."""
+    assert O.sink_end(226 + 13 * 30 * 45, 226, (13, 30, 45)) == 226 + 30 * 45
+    assert O.sink_end(75600, 0, (21, 45, 80)) == 45 * 80
+    assert O.sink_end(100, 100, (0, 4, 4)) == 100            # no video: the prefix only
+    assert O.sink_end(20, 4, (1, 4, 8)) == 20                 # one frame: everything
+
+
+def test_block_means_brute_force_and_tail():
+    """Block means equal a per-dim summation loop over the RoPE'd rows (3 text + 64 video tokens); the ragged block averages its 3 valid rows only."""
+    rng = _rng(31)
+    L, D, prefix, grid, split = 64 + 3, 16, 3, (1, 8, 8), (6, 5, 5)
+    x = rng.standard_normal((L, D)).astype(np.float16)
+    got = O.block_means(x, prefix, grid, split, 10000.0)
+    xr = O.apply_rope(x.astype(F32), prefix, grid, split, 10000.0)
+    for i, (a, b) in enumerate([(0, 64), (64, L)]):
+        for d in range(D):
+            acc = 0.0
+            for t in range(a, b):
+                acc += float(xr[t, d])
+            assert got[i, d] == pytest.approx(acc / (b - a), rel=1e-12, abs=1e-15)
+    # the ragged block is not diluted by the 61 padded rows
+    assert not np.allclose(got[1], xr[64:].astype(np.float64).sum(0) / 64, rtol=1e-3)
+
+
+def test_block_scores_are_tile_means_of_scores():
+    """S_hat[i, j] = q_hat_i . k_hat_j equals the mean of q_a . k_b over the tile (a in Q_i, b in K_j), by bilinearity."""
+    rng = _rng(32)
+    L, D, prefix, grid, split = 150, 16, 0, (1, 10, 15), (6, 5, 5)
+    q = rng.standard_normal((L, D)).astype(np.float16)
+    k = rng.standard_normal((L, D)).astype(np.float16)
+    s_hat = O.block_scores(O.block_means(q, prefix, grid, split, 10000.0), O.block_means(k, prefix, grid, split, 10000.0))
+    qr = O.apply_rope(q.astype(F32), prefix, grid, split, 10000.0).astype(np.float64)
+    kr = O.apply_rope(k.astype(F32), prefix, grid, split, 10000.0).astype(np.float64)
+    S = qr @ kr.T
+    nb = O.n_blocks(L)
+    for i in range(nb):
+        for j in range(nb):
+            tile = S[64 * i:min(L, 64 * i + 64), 64 * j:min(L, 64 * j + 64)]
+            assert s_hat[i, j] == pytest.approx(tile.mean(), rel=1e-10, abs=1e-12)
+
+
+def test_block_scores_invariant_under_hadamard():
+    """Means of the Hadamard-rotated rows give the same S_hat (the rotation is orthonormal and linear)."""
+    rng = _rng(33)
+    L, D, grid, split = 128, 128, (2, 8, 8), (44, 42, 42)
+    q = rng.standard_normal((L, D)).astype(np.float16)
+    k = rng.standard_normal((L, D)).astype(np.float16)
+    qm = O.block_means(q, 0, grid, split, 10000.0)
+    km = O.block_means(k, 0, grid, split, 10000.0)
+    H = BF.sylvester(D) / math.sqrt(D)
+    assert np.allclose(O.block_scores(qm @ H, km @ H), O.block_scores(qm, km), rtol=1e-10, atol=1e-12)
+
+
+def test_sparse_mask_rank_count_brute_force():
+    """Top-n per query block equals the rank-count rule (fewer than n keys rank above it, ties to lower j), plus the sink rows and columns."""
+    rng = _rng(34)
+    nb, n = 9, 3
+    s = rng.integers(-3, 4, (nb, nb)).astype(np.float64)     # many ties
+    L, prefix, grid = nb * 64, 10, (3, 10, 17)                # sink_end = 10 + 170 = 180 -> blocks 0..2
+    M = O.sparse_block_mask(s, n, L, prefix, grid)
+    for i in range(nb):
+        for j in range(nb):
+            rank = sum(1 for kk in range(nb) if s[i, kk] > s[i, j] or (s[i, kk] == s[i, j] and kk < j))
+            want = rank < n or j <= 2 or i <= 2
+            assert M[i, j] == want, (i, j)
+    assert M[:3].all() and M[:, :3].all()
+
+
+def test_sparse_mask_worked_example():
+    """Hand-checked: scores with a clear order select the expected blocks; topn >= NB keeps everything."""
+    s = np.array([[5., 1., 4., 2., 3.],
+                  [1., 2., 3., 4., 5.],
+                  [0., 0., 0., 0., 0.],
+                  [9., 8., 7., 6., 5.],
+                  [2., 9., 2., 9., 1.]])
+    L, prefix, grid = 5 * 64, 0, (5, 8, 8)                    # frame 0 = block 0 is the sink
+    M = O.sparse_block_mask(s, 2, L, prefix, grid)
+    want = np.array([[1, 1, 1, 1, 1],                         # sink query block
+                     [1, 0, 0, 1, 1],
+                     [1, 1, 0, 0, 0],                         # all equal: lowest j
+                     [1, 1, 0, 0, 0],
+                     [1, 1, 0, 1, 0]], dtype=bool)
+    assert np.array_equal(M, want)
+    assert O.sparse_block_mask(s, 5, L, prefix, grid).all()
+
+
+def test_sparse_forward_dense_mask_equals_dense_path():
+    """With every block kept the block-sparse path is the dense INT4 path (same loop, same codes)."""
+    w = W.WORKLOADS["tiny"]
+    x = W.head_inputs(w, 0, 1)
+    kw = dict(prefix=w.prefix, grid=w.grid, split=w.split, base=w.base, rotation=w.rotation)
+    nb = O.n_blocks(w.L)
+    sp = O.sparse_forward_head(x["q"], x["k"], x["v"], topn=nb, **kw)
+    dn = O.forward_head(x["q"], x["k"], x["v"], **kw)
+    assert sp["mask"].all()
+    assert np.array_equal(sp["out"], dn["out"])
+
+
+def test_sparse_forward_masked_softmax_identity():
+    """Unquantized, the block-skipping loop with a per-query-block mask equals softmax restricted to the kept keys."""
+    rng = _rng(35)
+    L, D = 200, 32
+    nb = O.n_blocks(L)
+    q, k, v = (rng.standard_normal((L, D)) for _ in range(3))
+    pad = lambda a: np.concatenate([a, np.zeros((nb * 64 - L, a.shape[1]))])
+    M = np.array([[1, 0, 1, 1], [0, 1, 0, 1], [1, 1, 1, 0], [0, 0, 1, 1]], dtype=bool)
+    ones = np.ones(nb, dtype=F32)
+    for qb in range(nb):
+        rows = np.arange(64 * qb, min(L, 64 * qb + 64), 7)
+        r = O.int4_flash_rows(pad(q), ones, pad(k), ones, pad(v), np.ones(D, F32), None, L, D, rows,
+                              key_blocks=M[qb], quantize_p=False)
+        keys = np.nonzero(np.repeat(M[qb], 64)[:L])[0]
+        want = BF.softmax_attention_brute(q[rows], k[keys], v[keys], 1.0 / math.sqrt(D))
+        assert np.allclose(r["O_scaled"] / r["l"][:, None], want, rtol=0, atol=2e-5)
+
+
+def test_sparse_sink_rows_are_dense():
+    """Query blocks that hold first-frame tokens keep every key block, so their outputs equal the dense path's."""
+    w = W.WORKLOADS["tiny"]
+    x = W.head_inputs(w, 0, 0)
+    kw = dict(prefix=w.prefix, grid=w.grid, split=w.split, base=w.base, rotation=w.rotation)
+    rows = np.arange(0, 64)                                   # frame 0 of the 4x8x8 grid = block 0
+    sp = O.sparse_forward_head(x["q"], x["k"], x["v"], topn=1, rows=rows, **kw)
+    dn = O.forward_head(x["q"], x["k"], x["v"], rows=rows, **kw)
+    assert not sp["mask"][1:, 1:].all()
+    assert np.array_equal(sp["out"], dn["out"])
