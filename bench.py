@@ -12,7 +12,14 @@ reports the INT4 attention kernel alone against the INT8 matrix-core peak
 whose dense peak is the same). The CPU baseline is the oracle (numpy) on a bounded
 sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+With --sparse F the step is the block-sparse path instead (RainFusion2.0
+sections 3.1-3.4): rotattn_quantize_qk with block sums -> rotattn_quantize_v ->
+rotattn_block_mask (top round(F * NB) key blocks per 128-row query block, plus
+the first-frame sink) -> rotattn_sparse_attention; `value` then counts the
+executed ops (4 D per kept score element) and the line also carries the
+density and the dense-equivalent rate.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p] [--sparse F]
 """
 from __future__ import annotations
 
@@ -94,6 +101,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time bound of the oracle baseline sample (whole 512-row chunks)")
+    ap.add_argument("--sparse", type=float, default=None, metavar="F",
+                    help="block-sparse path keeping the top round(F * NB) key blocks per 128-row query block")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (scales HBM traffic counters) and exit")
     args = ap.parse_args()
@@ -117,6 +126,8 @@ def main():
         return
 
     w = W.WORKLOADS[args.workload]
+    if args.sparse is not None:
+        return sparse_main(args, w)
     t_gen = time.perf_counter()
     x = W.full_inputs(w, threads=16)
     t_gen = time.perf_counter() - t_gen
@@ -188,6 +199,85 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(rec))
+
+
+def sparse_main(args, w):
+    """The block-sparse step (see the module docstring); one JSON line like main()'s."""
+    import torch
+
+    import int4_quantized_flashattention_amd as R
+    if np.isfinite(w.tau) or W.head_fallback_mask(w) is not None:
+        print(json.dumps({"error": f"workload {w.name} routes blocks to FP16; the block-sparse path has no FP16 "
+                                   "fallback"}))
+        sys.exit(2)
+    x = W.full_inputs(w, threads=16)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[t]).to(dev) for t in ("q", "k", "v"))
+    p = R.problem_from_workload(w)
+    s = R.get_sizes(p)
+    topn = max(1, int(round(args.sparse * s.NB)))
+    qk = R.binding.alloc_qk(p, dev, False, block_sums=True)
+    vq = R.binding.alloc_v(p, dev)
+    mask = torch.empty((w.B, w.H, s.mask_rows, s.mask_words), dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.H, w.L, w.D), dtype=torch.float16, device=dev)
+    ws = {c: torch.empty(max(1, R.workspace_bytes(p, c)), dtype=torch.uint8, device=dev)
+          for c in (R.binding.CALL_QUANTIZE_QK, R.binding.CALL_QUANTIZE_V, R.binding.CALL_SPARSE_ATTENTION)}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        R.rotattn_quantize_qk(p, q, k, out=qk, ws=ws[R.binding.CALL_QUANTIZE_QK], stream=stream)
+        R.rotattn_quantize_v(p, v, out=vq, ws=ws[R.binding.CALL_QUANTIZE_V], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        R.rotattn_block_mask(p, qk, topn, out=mask, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        R.rotattn_sparse_attention(p, qk, vq, mask, out=out, ws=ws[R.binding.CALL_SPARSE_ATTENTION], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pro = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_mask = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_att = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_per_step = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
+    bits = R.mask_to_bool(mask.cpu().numpy().astype(np.uint32), s.NB)   # [B, H, rows, NB]
+    rows = np.minimum(128, w.L - 128 * np.arange(s.mask_rows))
+    keys = np.minimum(64, w.L - 64 * np.arange(s.NB))
+    kept_scores = float(np.einsum("bhij,i,j->", bits.astype(np.float64), rows.astype(np.float64),
+                                  keys.astype(np.float64)))
+    density = kept_scores / (w.B * w.H * float(w.L) * w.L)
+    ops = 4.0 * kept_scores * w.D
+    achieved = ops / (t_att * 1e-3) / 1e12
+    rec = {
+        "metric": "block-sparse attention TOPS executed (4 D per kept score element) and % of INT8 MFMA peak",
+        "value": round(ops / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i4", "data": "synthetic",
+        "config": {"workload": f"{w.name} block-sparse: B={w.B} H={w.H} L={w.L} D={w.D} "
+                               f"grid={'x'.join(map(str, w.grid))} topn={topn} of NB={s.NB}",
+                   "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.D, "parallelism": "none"},
+        "density": round(density, 4),
+        "dense_equivalent_TOPS": round(w.credited_ops() / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "int4_attn_kernel, block-sparse (rotattn_sparse_attention)", "avg_ms": round(t_att, 4)},
+        "breakdown_ms": {"quantize_qk_and_v": round(t_pro, 4), "block_mask": round(t_mask, 4),
+                         "sparse_attention": round(t_att, 4)},
+        "wall_s_timed": round(wall, 3),
+    }
     print(json.dumps(rec))
 
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ROTATTN_VERSION 3
+#define ROTATTN_VERSION 4
 
 /* error codes */
 #define ROTATTN_OK            0
@@ -63,6 +63,8 @@ extern "C" {
 #define ROTATTN_CALL_FORWARD     3
 #define ROTATTN_CALL_FP16_FORWARD 4
 #define ROTATTN_CALL_DEBUG_DUMP  5
+#define ROTATTN_CALL_BLOCK_MASK  6
+#define ROTATTN_CALL_SPARSE_ATTENTION 7
 
 typedef void* rotattn_stream_t; /* hipStream_t */
 
@@ -90,6 +92,10 @@ typedef struct rotattn_qk_buffers {
   uint32_t* head_kflag; /* [B*H] nonzero if any K block of the head is flagged */
   void* q_rope;         /* optional fp16 [B][H][L][D] (dense): RoPE'd, unrotated Q for the FP16 path; NULL = not written */
   void* k_rope;         /* optional, as q_rope */
+  float* q_bsum;        /* optional float [B][H][NB][D] (16-byte aligned): per 64-token block, the sum of the RoPE'd,
+                           unrotated rows over the block's valid tokens (float32, ascending token order); the input
+                           of rotattn_block_mask; NULL = not written */
+  float* k_bsum;        /* optional, as q_bsum */
 } rotattn_qk_buffers;
 
 /* Quantized V. All device. */
@@ -112,6 +118,10 @@ typedef struct rotattn_sizes {
   int64_t rope_bytes;      /* each of q_rope, k_rope */
   int64_t v_codes_bytes, v_scale_bytes, v_colsum_bytes;
   int64_t out_min_elems;   /* smallest element count an output buffer with the problem's strides spans */
+  int64_t bsum_bytes;      /* each of q_bsum, k_bsum */
+  int64_t mask_rows;       /* 128-row query blocks of a block-sparse mask: ceil(NB / 2) */
+  int64_t mask_words;      /* uint32 words per mask row: ceil(NB / 32) */
+  int64_t mask_bytes;      /* block-sparse mask [B][H][mask_rows][mask_words] uint32 */
 } rotattn_sizes;
 
 /* Library version (ROTATTN_VERSION). */
@@ -131,7 +141,8 @@ int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes);
  * pair turned by pos * base^(-2i/g_rot) of its axis group), the
  * Walsh-Hadamard rotation, symmetric INT4 quantization per 64-token block
  * (s = absmax/7, codes clamp(rne(x/s), -7, 7)) and the block error flags
- * (NSR = |x - s c|^2 / |x|^2 > block_err_tau).
+ * (NSR = |x - s c|^2 / |x|^2 > block_err_tau); optionally the RoPE'd block
+ * sums of block-sparse attention (out->q_bsum, out->k_bsum).
  * q, k: device fp16 with the problem's strides, 16-byte aligned rows.
  * out: codes, scales, flags, head_kflag (all required); q_rope/k_rope
  * optional (required later by rotattn_attention when FP16 fallback can occur).
@@ -204,12 +215,58 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
  *                                      (= pq . v + 8 * colsum)
  *   m_hist  float [n_units][64][NB]   running max (log2 domain) after each block
  * Rows at or beyond L are not written. head_fallback as in rotattn_attention.
+ * block_mask: NULL (dense) or a block-sparse mask as in
+ * rotattn_sparse_attention (then head_fallback must be NULL and
+ * block_err_tau +inf; key blocks the mask drops stay untouched).
  * Workspace: ROTATTN_CALL_DEBUG_DUMP bytes (the K/V block images).
  */
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
-                       const uint8_t* head_fallback, const int32_t* units, int32_t n_units,
+                       const uint8_t* head_fallback, const uint32_t* block_mask, const int32_t* units,
+                       int32_t n_units,
                        int32_t* acc_qk, int8_t* p_codes, int32_t* acc_pv, float* m_hist,
                        void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
+
+/*
+ * Block mask of block-sparse attention (RainFusion2.0, sec. 3.2
+ * "Representative Token for Blocks" and sec. 3.4 "First Frame Sink").
+ * Query blocks of 128 rows, key blocks of 64 keys (sec. 3.1 lets the two
+ * block sizes differ; 128 rows are one workgroup of the INT4 kernel).
+ * Representative tokens: the mean of every block of the RoPE'd (unrotated) Q
+ * and K over the block's valid tokens, from the block sums rotattn_quantize_qk
+ * writes into qk->q_bsum / qk->k_bsum (a 128-row query block adds its two
+ * sums; each sum is divided by its row count in float32). For query block i,
+ * S_hat[i][j] = q_hat_i . k_hat_j (one float32 fma chain over the head dim);
+ * the topn key blocks with the largest S_hat are kept (equal scores: lower j
+ * first), then every key block holding a text-prefix or first-frame token
+ * (tokens below text_prefix + grid_h * grid_w) is kept, and a query block
+ * holding such a token keeps every key block.
+ * qk: the buffers of rotattn_quantize_qk; only q_bsum and k_bsum are read
+ * (required).
+ * topn >= 1 (topn >= NB keeps everything).
+ * mask: device uint32 [B][H][mask_rows][mask_words] (rotattn_sizes), 4-byte
+ *   aligned: bit (j % 32) of word j / 32 of row (b, h, i) = 1 iff key block j
+ *   is kept for query rows [128 i, 128 i + 128); bits at or beyond NB are 0.
+ * Errors: EINVAL (null pointer, topn < 1), EUNSUPPORTED (NB > 16384 or
+ * B*H > 65535), EALIGN.
+ * Workspace: none (ROTATTN_CALL_BLOCK_MASK is 0 bytes; NULL is accepted).
+ */
+int rotattn_block_mask(const rotattn_problem* p, const rotattn_qk_buffers* qk, int32_t topn, uint32_t* mask,
+                       void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
+
+/*
+ * Block-sparse INT4 attention (RainFusion2.0, sec. 3.1 "Blockwise Sparse":
+ * Q_i K_j^T and P_ij V_j are skipped where M_ij = 0): the INT4 flash loop of
+ * rotattn_attention over the key blocks the mask keeps for each query block,
+ * in ascending order. block_mask as written by rotattn_block_mask (any mask
+ * of that layout is accepted; a query block that keeps no key block gets
+ * zeros). Block routing does not combine with it: block_err_tau must be
+ * +inf (else EINVAL); there is no FP16 fallback on this call.
+ * out: device fp16 with the problem's strides.
+ * Workspace: ROTATTN_CALL_SPARSE_ATTENTION bytes (the K/V block images).
+ */
+int rotattn_sparse_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
+                             const uint32_t* block_mask, void* out, void* workspace, size_t workspace_bytes,
+                             rotattn_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ from . import binding  # noqa: F401
 from .binding import (  # noqa: F401
     ROT_FULL, ROT_GROUP64, Problem, QKCodes, VCodes, RotattnError, make_problem, problem_from_workload,
     get_sizes, workspace_bytes, rotattn_quantize_qk, rotattn_quantize_v, rotattn_attention, rotattn_forward,
-    rotattn_fp16_forward, rotattn_debug_dump, load_library,
+    rotattn_fp16_forward, rotattn_debug_dump, rotattn_block_mask, rotattn_sparse_attention, mask_to_bool,
+    load_library,
 )
 
 __all__ = [n for n in dir() if n.startswith("rotattn_") or n in (

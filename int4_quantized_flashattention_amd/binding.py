@@ -23,13 +23,15 @@ CALL_ATTENTION = 2
 CALL_FORWARD = 3
 CALL_FP16_FORWARD = 4
 CALL_DEBUG_DUMP = 5
+CALL_BLOCK_MASK = 6
+CALL_SPARSE_ATTENTION = 7
 
 ERRORS = {0: "ROTATTN_OK", -1: "ROTATTN_EINVAL", -2: "ROTATTN_EUNSUPPORTED", -3: "ROTATTN_EALIGN",
           -4: "ROTATTN_EWORKSPACE", -5: "ROTATTN_ELAUNCH"}
 
 EXPORTS = ["rotattn_version", "rotattn_strerror", "rotattn_get_sizes", "rotattn_workspace_bytes",
            "rotattn_quantize_qk", "rotattn_quantize_v", "rotattn_attention", "rotattn_forward",
-           "rotattn_fp16_forward", "rotattn_debug_dump"]
+           "rotattn_fp16_forward", "rotattn_debug_dump", "rotattn_block_mask", "rotattn_sparse_attention"]
 
 
 class Problem(C.Structure):
@@ -43,7 +45,8 @@ class Problem(C.Structure):
 class QKBuffers(C.Structure):
     _fields_ = [("q_codes", C.c_void_p), ("k_codes", C.c_void_p), ("q_scale", C.c_void_p),
                 ("k_scale", C.c_void_p), ("q_flag", C.c_void_p), ("k_flag", C.c_void_p),
-                ("head_kflag", C.c_void_p), ("q_rope", C.c_void_p), ("k_rope", C.c_void_p)]
+                ("head_kflag", C.c_void_p), ("q_rope", C.c_void_p), ("k_rope", C.c_void_p),
+                ("q_bsum", C.c_void_p), ("k_bsum", C.c_void_p)]
 
 
 class VBuffers(C.Structure):
@@ -53,7 +56,8 @@ class VBuffers(C.Structure):
 class Sizes(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("Lp", "NB", "Dp", "qk_codes_bytes", "qk_scale_bytes", "qk_flag_bytes",
                                          "head_flag_bytes", "rope_bytes", "v_codes_bytes", "v_scale_bytes",
-                                         "v_colsum_bytes", "out_min_elems")]
+                                         "v_colsum_bytes", "out_min_elems", "bsum_bytes", "mask_rows", "mask_words",
+                                         "mask_bytes")]
 
 
 _lib = None
@@ -79,8 +83,10 @@ def load_library(path: str = LIB_PATH):
     lib.rotattn_attention.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_forward.argtypes = [P(Problem), P(QKBuffers), vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_fp16_forward.argtypes = [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp]
-    lib.rotattn_debug_dump.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, C.c_int32,
+    lib.rotattn_debug_dump.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, vp, C.c_int32,
                                        vp, vp, vp, vp, vp, C.c_size_t, vp]
+    lib.rotattn_block_mask.argtypes = [P(Problem), P(QKBuffers), C.c_int32, vp, vp, C.c_size_t, vp]
+    lib.rotattn_sparse_attention.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, vp, C.c_size_t, vp]
     for name in EXPORTS:
         if name not in ("rotattn_strerror",):
             getattr(lib, name).restype = C.c_int
@@ -184,6 +190,8 @@ class QKCodes:
     head_kflag: object
     q_rope: object = None
     k_rope: object = None
+    q_bsum: object = None
+    k_bsum: object = None
 
     def struct(self) -> QKBuffers:
         s = QKBuffers()
@@ -206,7 +214,7 @@ class VCodes:
         return s
 
 
-def alloc_qk(p: Problem, device, rope_copy: bool) -> QKCodes:
+def alloc_qk(p: Problem, device, rope_copy: bool, block_sums: bool = False) -> QKCodes:
     torch = _torch()
     s = get_sizes(p)
     B, H = p.B, p.H
@@ -221,6 +229,8 @@ def alloc_qk(p: Problem, device, rope_copy: bool) -> QKCodes:
         head_kflag=torch.empty((B * H,), dtype=torch.int32, device=device),
         q_rope=torch.empty((B, H, p.L, p.D), dtype=torch.float16, device=device) if rope_copy else None,
         k_rope=torch.empty((B, H, p.L, p.D), dtype=torch.float16, device=device) if rope_copy else None,
+        q_bsum=torch.empty((B, H, s.NB, p.D), dtype=f32, device=device) if block_sums else None,
+        k_bsum=torch.empty((B, H, s.NB, p.D), dtype=f32, device=device) if block_sums else None,
     )
 
 
@@ -234,10 +244,12 @@ def alloc_v(p: Problem, device) -> VCodes:
     )
 
 
-def rotattn_quantize_qk(p: Problem, q, k, out: QKCodes = None, rope_copy: bool = False, ws=None, stream=None):
-    """RoPE + rotation + per-block INT4 quantization of Q and K (see include/rotattn.h)."""
+def rotattn_quantize_qk(p: Problem, q, k, out: QKCodes = None, rope_copy: bool = False, ws=None, stream=None,
+                        block_sums: bool = False):
+    """RoPE + rotation + per-block INT4 quantization of Q and K (see include/rotattn.h); block_sums also writes
+    the RoPE'd block sums that rotattn_block_mask reads."""
     if out is None:
-        out = alloc_qk(p, q.device, rope_copy)
+        out = alloc_qk(p, q.device, rope_copy, block_sums)
     ws, n = _workspace(p, CALL_QUANTIZE_QK, q.device, ws)
     st = out.struct()
     _check(load_library().rotattn_quantize_qk(C.byref(p), _ptr(q), _ptr(k), C.byref(st), _ptr(ws), n,
@@ -289,7 +301,45 @@ def rotattn_fp16_forward(p: Problem, q, k, v, out=None, ws=None, stream=None):
     return out
 
 
-def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback=None, ws=None, stream=None):
+def rotattn_block_mask(p: Problem, qk: QKCodes, topn: int, out=None, ws=None, stream=None):
+    """Block-sparse mask from the block sums of rotattn_quantize_qk(block_sums=True) (see include/rotattn.h):
+    int32 view of uint32 [B, H, mask_rows, mask_words], one row per 128 query rows."""
+    torch = _torch()
+    s = get_sizes(p)
+    dev = qk.q_codes.device
+    if out is None:
+        out = torch.empty((p.B, p.H, s.mask_rows, s.mask_words), dtype=torch.int32, device=dev)
+    ws, n = _workspace(p, CALL_BLOCK_MASK, dev, ws)
+    qs = qk.struct()
+    _check(load_library().rotattn_block_mask(C.byref(p), C.byref(qs), int(topn), _ptr(out), _ptr(ws), n,
+                                             _stream(stream)), "rotattn_block_mask")
+    return out
+
+
+def rotattn_sparse_attention(p: Problem, qk: QKCodes, vq: VCodes, block_mask, out=None, ws=None, stream=None):
+    """Block-sparse INT4 attention over the key blocks `block_mask` keeps (see include/rotattn.h)."""
+    torch = _torch()
+    dev = qk.q_codes.device
+    if out is None:
+        out = torch.empty((p.B, p.H, p.L, p.D), dtype=torch.float16, device=dev)
+    ws, n = _workspace(p, CALL_SPARSE_ATTENTION, dev, ws)
+    qs, vs = qk.struct(), vq.struct()
+    _check(load_library().rotattn_sparse_attention(C.byref(p), C.byref(qs), C.byref(vs), _ptr(block_mask),
+                                                   _ptr(out), _ptr(ws), n, _stream(stream)),
+           "rotattn_sparse_attention")
+    return out
+
+
+def mask_to_bool(mask_words, NB: int):
+    """Host helper: int32/uint32 words [..., rows, mask_words] -> bool [..., rows, NB]."""
+    import numpy as np
+    w = np.asarray(mask_words).astype(np.uint32)
+    bits = (w[..., :, :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    return bits.reshape(w.shape[:-1] + (w.shape[-1] * 32,))[..., :NB].astype(bool)
+
+
+def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback=None, ws=None, stream=None,
+                       block_mask=None):
     """Intermediate integers of the INT4 kernel for 64-row query blocks `units` ((b*H+h)*NB + block)."""
     torch = _torch()
     dev = qk.q_codes.device
@@ -303,7 +353,8 @@ def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback
     ws, nws = _workspace(p, CALL_DEBUG_DUMP, dev, ws)
     qs, vs = qk.struct(), vq.struct()
     _check(load_library().rotattn_debug_dump(C.byref(p), C.byref(qs), C.byref(vs), _ptr(head_fallback),
-                                             _ptr(units), n, _ptr(acc), _ptr(pq), _ptr(pv), _ptr(m),
+                                             _ptr(block_mask), _ptr(units), n, _ptr(acc), _ptr(pq), _ptr(pv),
+                                             _ptr(m),
                                              _ptr(ws), nws, _stream(stream)), "rotattn_debug_dump")
     return {"acc": acc, "pq": pq, "accpv": pv, "m": m}
 
@@ -315,3 +366,5 @@ attention = rotattn_attention
 forward = rotattn_forward
 fp16_forward = rotattn_fp16_forward
 debug_dump = rotattn_debug_dump
+block_mask = rotattn_block_mask
+sparse_attention = rotattn_sparse_attention

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librotattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["prologue.hip", "vquant.hip", "attn_int4.hip", "attn_fp16.hip", "rotattn_api.hip"]
+SOURCES = ["prologue.hip", "vquant.hip", "attn_int4.hip", "attn_fp16.hip", "sparse_mask.hip", "rotattn_api.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -132,7 +132,10 @@ constexpr int kFp6 = 2;
 // queries (FP6 products), the online softmax and P codes in registers, and
 // O^T on the FP8 matrix cores into a float32 accumulator kept at the running
 // max, rescaled only when some row max of the wave grows.
-template <int DP, int DV, int NW, int NST, int OCC, bool DUMP>
+// SPARSE: block-sparse attention (RainFusion2.0, section 3.1: Q_i K_j^T and
+// P_ij V_j are skipped where M_ij = 0), with one mask row per 128-row query
+// block: the loop visits only the key blocks that row keeps.
+template <int DP, int DV, int NW, int NST, int OCC, bool DUMP, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
   constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP8 product each)
@@ -231,12 +234,30 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   }
 
   const uint8_t* kflag = a.route ? a.k_flag + (long long)bh * NB : nullptr;
+  // Block-sparse: the bit row (words of 32 key blocks) of the 128-row query
+  // block this workgroup covers; every wave processes exactly the key blocks
+  // the loop visits.
+  const int MW = a.mask_words;
+  const uint32_t* mrow = nullptr;
+  if constexpr (SPARSE) mrow = a.block_mask + ((long long)bh * ((NB + 1) / 2) + row_base / kMaskQBlock) * MW;
   // the next key block at or after j that this path takes (NB if none); the
   // result is wave-uniform, which keeps the loop control in scalar registers
   auto next_block = [&](int j) __attribute__((always_inline)) {
-    if (kflag != nullptr)
-      while (j < NB && uniform_byte(kflag, j) != 0) ++j;   // FP16 tile: the other path takes it
-    return __builtin_amdgcn_readfirstlane(j);
+    if constexpr (SPARSE) {
+      if (j >= NB) return NB;
+      int w = j >> 5;
+      uint32_t bits = uniform_word(mrow, w) & (~0u << (j & 31));
+      while (bits == 0) {
+        if (++w >= MW) return NB;
+        bits = uniform_word(mrow, w);
+      }
+      j = __builtin_amdgcn_readfirstlane(32 * w + __builtin_ctz(bits));
+      return j < NB ? j : NB;
+    } else {
+      if (kflag != nullptr)
+        while (j < NB && uniform_byte(kflag, j) != 0) ++j;   // FP16 tile: the other path takes it
+      return __builtin_amdgcn_readfirstlane(j);
+    }
   };
   // Block j's image goes to LDS stage `stage` with NDMA direct-to-LDS loads per
   // thread: thread t copies bytes 16t + 4096i of the image, and the hardware
@@ -509,8 +530,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   if (row >= L) return;
   const float* svp = a.v_scale + (long long)bh * DV;
   if (!mixed) {
-    // out = O (s_v / 15) / l with O = 2^9 o and l = l15 / 15
-    const float inv = 512.0f / l15t;
+    // out = O (s_v / 15) / l with O = 2^9 o and l = l15 / 15 (a sparse row
+    // that keeps no key block gets zeros)
+    const float inv = (SPARSE && l15t == 0.f) ? 0.f : 512.0f / l15t;
     __half* orow = a.out + (long long)b * kp.sb + (long long)h * kp.sh + (long long)row * kp.sl;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -560,19 +582,28 @@ struct Shape {
   static constexpr int kStages = (kOcc * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3;
 };
 
-template <int DP, int DV>
-static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump, float c0, float l15,
-                                hipStream_t s) {
+template <int DP, int DV, bool SPARSE>
+static void launch_int4_s(const KProblem& kp, const AttnArgs& a, bool dump, float c0, float l15, hipStream_t s) {
   using S = Shape<DP, DV>;
   constexpr int W = S::kWaves, NS = S::kStages, OC = S::kOcc;
   if (dump) {
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true>), dim3(a.n_units), dim3(W * 64), 0, s, kp, a,
-                       c0, l15);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true, SPARSE>), dim3(a.n_units), dim3(W * 64), 0, s,
+                       kp, a, c0, l15);
   } else {
     const int ntiles = (kp.L + 32 * W - 1) / (32 * W);
     dim3 grid(ntiles * kp.H * kp.B);
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false>), grid, dim3(W * 64), 0, s, kp, a, c0, l15);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false, SPARSE>), grid, dim3(W * 64), 0, s, kp, a, c0,
+                       l15);
   }
+}
+
+template <int DP, int DV>
+static hipError_t launch_int4_t(const KProblem& kp, const AttnArgs& a, bool dump, float c0, float l15,
+                                hipStream_t s) {
+  if (a.block_mask != nullptr)
+    launch_int4_s<DP, DV, true>(kp, a, dump, c0, l15, s);
+  else
+    launch_int4_s<DP, DV, false>(kp, a, dump, c0, l15, s);
   return hipGetLastError();
 }
 

@@ -125,6 +125,16 @@ __device__ __forceinline__ uint32_t uniform_byte(const uint8_t* base, int i) {
   return (w >> (8 * (lo & 3u))) & 0xFFu;
 }
 
+// Word i of a uint32 array that no thread writes during the kernel, for a
+// wave-uniform base and i, through the scalar unit (see uniform_byte).
+__device__ __forceinline__ uint32_t uniform_word(const uint32_t* base, int i) {
+  const uint64_t addr = reinterpret_cast<uintptr_t>(base + i);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
+  return *reinterpret_cast<const_u32p>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
@@ -144,6 +154,7 @@ struct QKOut {
   uint8_t* q_flag; uint8_t* k_flag;
   uint32_t* head_kflag;
   __half* q_rope; __half* k_rope;
+  float* q_bsum; float* k_bsum;   // optional 64-token block sums of the RoPE'd rows [B*H][NB][D]
 };
 struct VOut {
   uint8_t* v_codes; float* v_scale; int32_t* v_colsum;
@@ -157,6 +168,8 @@ struct AttnArgs {
   const uint8_t* v_codes; const float* v_scale;
   const uint8_t* kv_image;      // [B*H][NB] LDS images of the K/V blocks (kv_image_bytes each)
   const uint8_t* f16_vt;        // [B*H][NB] V^T blocks of the FP16 path (128 * D bytes each)
+  const uint32_t* block_mask;   // block-sparse: [B*H][ceil(NB/2)][mask_words] key-block bits per 128-row query block
+  int mask_words;               // ceil(NB / 32)
   const __half* q_rope; const __half* k_rope; const __half* v;   // FP16 path inputs
   __half* out;
   float* part_o; float* part_m; float* part_l;   // INT4 partials of mixed rows [B][H][Lp][D], [B][H][Lp]
@@ -173,6 +186,10 @@ hipError_t launch_rope_copy(const KProblem& kp, const __half* x, const float* ta
 hipError_t launch_vquant(const KProblem& kp, const __half* v, uint32_t* absmax_bits, const VOut& o, hipStream_t s);
 hipError_t launch_kv_image(const KProblem& kp, const AttnArgs& a, uint8_t* image, hipStream_t s);
 hipError_t launch_int4_attention(const KProblem& kp, const AttnArgs& a, bool dump, hipStream_t s);
+hipError_t launch_block_topn(const KProblem& kp, const float* q_bsum, const float* k_bsum, int topn, int sink_rows,
+                             int sink_cols, uint32_t* mask, hipStream_t s);
+constexpr int kMaxMaskBlocks = 16384;   // largest NB the block-mask builder takes (L <= 1048576)
+constexpr int kMaskQBlock = 128;        // query rows per block-sparse mask row (one INT4 workgroup)
 hipError_t launch_fp16_vt(const KProblem& kp, const __half* v, uint8_t* image, hipStream_t s);
 hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, bool whole_call, hipStream_t s);
 }  // namespace rotattn

@@ -156,6 +156,19 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
   __syncthreads();
   __half* rcopy = tensor ? o.k_rope : o.q_rope;
   if (rcopy != nullptr) store_rope_copy<D>(kp, b, h, blk, Y, rcopy);
+  // block sum of the RoPE'd rows over the valid tokens (ascending order), the
+  // representative token of block-sparse attention before its division by the
+  // count (RainFusion2.0, section 3.2)
+  float* bsum = tensor ? o.k_bsum : o.q_bsum;
+  if (bsum != nullptr) {
+    const int n = min(kBlock, kp.L - blk * kBlock);
+    float* dst = bsum + ((long long)(b * kp.H + h) * kp.NB + blk) * D;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      float acc = 0.f;
+      for (int t = 0; t < n; ++t) acc = fadd_rn(acc, Y[t][d]);
+      dst[d] = acc;
+    }
+  }
 
   // Walsh-Hadamard on 32-value chunks: stages 1..16 in registers, 32 and 64 across lanes.
   float v[ROUNDS][32];
@@ -254,6 +267,7 @@ __global__ __launch_bounds__(256) void rope_copy_kernel(KProblem kp, const __hal
   __syncthreads();
   store_rope_copy<D>(kp, b, h, blk, Y, dst);
 }
+
 
 hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, hipStream_t s) {
   int entries = 0;

@@ -5,6 +5,7 @@
 #include "../../include/rotattn.h"
 #include "common.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -119,7 +120,10 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
       L.tab = take(tab_bytes); L.qr = take(rope_b); L.kr = take(rope_b); L.vt = take(vt_b);
       break;
     case ROTATTN_CALL_DEBUG_DUMP:
+    case ROTATTN_CALL_SPARSE_ATTENTION:
       L.img = take(img_b);
+      break;
+    case ROTATTN_CALL_BLOCK_MASK:   // no scratch
       break;
     default:
       break;
@@ -233,6 +237,10 @@ int rotattn_get_sizes(const rotattn_problem* p, rotattn_sizes* out) {
   out->v_codes_bytes = BH * d.NB * p->D * 32;
   out->v_scale_bytes = BH * p->D * 4;
   out->v_colsum_bytes = BH * d.NB * p->D * 4;
+  out->bsum_bytes = BH * d.NB * p->D * 4;
+  out->mask_rows = (d.NB + 1) / 2;
+  out->mask_words = (d.NB + 31) / 32;
+  out->mask_bytes = BH * out->mask_rows * out->mask_words * 4;
   out->out_min_elems = (p->L == 0) ? 0
       : (int64_t)(p->B - 1) * p->stride_b + (int64_t)(p->H - 1) * p->stride_h + (int64_t)(p->L - 1) * p->stride_l + p->D;
   return ROTATTN_OK;
@@ -242,7 +250,7 @@ int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes) {
   Derived d;
   const int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
-  if (bytes == nullptr || call < 0 || call > ROTATTN_CALL_DEBUG_DUMP) return ROTATTN_EINVAL;
+  if (bytes == nullptr || call < 0 || call > ROTATTN_CALL_SPARSE_ATTENTION) return ROTATTN_EINVAL;
   *bytes = layout(p, d, call).total;
   return ROTATTN_OK;
 }
@@ -270,6 +278,8 @@ int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k, 
   o.head_kflag = out->head_kflag;
   o.q_rope = static_cast<__half*>(out->q_rope);
   o.k_rope = static_cast<__half*>(out->k_rope);
+  o.q_bsum = out->q_bsum;
+  o.k_bsum = out->k_bsum;
   return launched(launch_qk_prologue(d.kp, static_cast<const __half*>(q), static_cast<const __half*>(k), tab, o, s));
 }
 
@@ -359,7 +369,8 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
 }
 
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
-                       const uint8_t* head_fallback, const int32_t* units, int32_t n_units, int32_t* acc_qk,
+                       const uint8_t* head_fallback, const uint32_t* block_mask, const int32_t* units,
+                       int32_t n_units, int32_t* acc_qk,
                        int8_t* p_codes, int32_t* acc_pv, float* m_hist, void* workspace, size_t workspace_bytes,
                        rotattn_stream_t stream) {
   Derived d;
@@ -369,6 +380,10 @@ int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, c
   if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
   if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
   if (n_units < 0 || (n_units > 0 && (!units || !acc_qk || !p_codes || !acc_pv || !m_hist))) return ROTATTN_EINVAL;
+  if (block_mask != nullptr) {
+    if (((uintptr_t)block_mask & 3) != 0) return ROTATTN_EALIGN;
+    if (routes(p) || head_fallback != nullptr) return ROTATTN_EINVAL;
+  }
   const Layout L = layout(p, d, ROTATTN_CALL_DEBUG_DUMP);
   if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
   if (n_units == 0 || p->L == 0) return ROTATTN_OK;
@@ -382,11 +397,65 @@ int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, c
   a.route = routes(p);
   a.units = units; a.n_units = n_units;
   a.d_acc = acc_qk; a.d_pq = p_codes; a.d_pv = acc_pv; a.d_m = m_hist;
+  a.block_mask = block_mask;
+  a.mask_words = (int)((d.NB + 31) / 32);
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* img = at<uint8_t>(workspace, L.img);
   a.kv_image = img;
   if ((rc = launched(launch_kv_image(d.kp, a, img, s))) != ROTATTN_OK) return rc;
   return launched(launch_int4_attention(d.kp, a, true, s));
+}
+
+int rotattn_block_mask(const rotattn_problem* p, const rotattn_qk_buffers* qk, int32_t topn, uint32_t* mask,
+                       void* workspace, size_t workspace_bytes, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
+  if (qk == nullptr || qk->q_bsum == nullptr || qk->k_bsum == nullptr || mask == nullptr || topn < 1)
+    return ROTATTN_EINVAL;
+  if (d.NB > kMaxMaskBlocks || (int64_t)p->B * p->H > 65535) return ROTATTN_EUNSUPPORTED;
+  if (!aligned16(qk->q_bsum) || !aligned16(qk->k_bsum)) return ROTATTN_EALIGN;
+  if (((uintptr_t)mask & 3) != 0) return ROTATTN_EALIGN;
+  const Layout L = layout(p, d, ROTATTN_CALL_BLOCK_MASK);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  // text prefix + first frame: the tokens that take part in full attention
+  const int64_t frame = (p->grid_t > 0) ? (int64_t)p->grid_h * p->grid_w : 0;
+  const int64_t sink_end = std::min<int64_t>(p->L, (int64_t)p->text_prefix + frame);
+  const int sink_rows = (int)((sink_end + kMaskQBlock - 1) / kMaskQBlock);
+  const int sink_cols = (int)((sink_end + kBlock - 1) / kBlock);
+  return launched(launch_block_topn(d.kp, qk->q_bsum, qk->k_bsum, topn, sink_rows, sink_cols, mask,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int rotattn_sparse_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
+                             const uint32_t* block_mask, void* out, void* workspace, size_t workspace_bytes,
+                             rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != ROTATTN_OK) return rc;
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
+  if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
+  if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
+  if (block_mask == nullptr || out == nullptr || routes(p)) return ROTATTN_EINVAL;
+  if (((uintptr_t)block_mask & 3) != 0 || !aligned16(out)) return ROTATTN_EALIGN;
+  const Layout L = layout(p, d, ROTATTN_CALL_SPARSE_ATTENTION);
+  if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_codes = qk->q_codes; a.k_codes = qk->k_codes;
+  a.q_scale = qk->q_scale; a.k_scale = qk->k_scale;
+  a.q_flag = qk->q_flag; a.k_flag = qk->k_flag; a.head_kflag = qk->head_kflag;
+  a.v_codes = vq->v_codes; a.v_scale = vq->v_scale;
+  a.out = static_cast<__half*>(out);
+  a.route = false;
+  a.block_mask = block_mask;
+  a.mask_words = (int)((d.NB + 31) / 32);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* img = at<uint8_t>(workspace, L.img);
+  a.kv_image = img;
+  if ((rc = launched(launch_kv_image(d.kp, a, img, s))) != ROTATTN_OK) return rc;
+  return launched(launch_int4_attention(d.kp, a, false, s));
 }
 
 }  // extern "C"

@@ -27,9 +27,9 @@ What it computes, step by step, in the pages' order:
      section 3.1 (a tile is skipped by one path and computed by the other),
      and a log-sum-exp merge of the two partial results.
   6. Block-sparse attention (RainFusion2.0 sections 3.1, 3.2, 3.4): block
-     means as representative tokens, top-n key blocks per query block by
-     the score of the means, the first-frame sink on top, and the INT4 loop
-     over the kept key blocks only.
+     means as representative tokens (query blocks of 128 rows, key blocks of
+     64), top-n key blocks per query block by the score of the means, the
+     first-frame sink on top, and the INT4 loop over the kept key blocks.
 
 Floating point: every step that decides an integer (a Q/K/V code, a block
 flag, a P code) is evaluated in float32 with the operation order stated in each
@@ -487,23 +487,30 @@ def sink_end(L: int, prefix: int, grid) -> int:
     return min(L, prefix + (Hh * W if T > 0 else 0))
 
 
-def block_means(x16, prefix, grid, split, base) -> np.ndarray:
-    """Representative token of every 64-token block (RainFusion2.0 section 3.2).
+def block_means(x16, prefix, grid, split, base, size: int = BLOCK) -> np.ndarray:
+    """Representative token of every block of `size` tokens (RainFusion2.0 section 3.2).
 
     The block mean of the RoPE'd rows (RoPE in float32 as in apply_rope),
     averaged in float64 over the block's valid tokens (a ragged last block
     averages only its tokens below L). Reading: the means are taken on the
     RoPE'd Q and K, the vectors whose products the attention scores are;
     the Hadamard rotation would not change any score (it is orthonormal).
-    Returns float64 [NB, D].
+    Returns float64 [ceil(L / size), D].
     """
     xr = apply_rope(x16.astype(F32), prefix, grid, split, base)
     L, D = xr.shape
-    nb = n_blocks(L)
+    nb = -(-L // size)
     out = np.zeros((nb, D), dtype=F64)
     for i in range(nb):
-        out[i] = xr[i * BLOCK:min(L, (i + 1) * BLOCK)].astype(F64).mean(axis=0)
+        out[i] = xr[i * size:min(L, (i + 1) * size)].astype(F64).mean(axis=0)
     return out
+
+
+# Query and key block sizes of the block-sparse mask. RainFusion2.0 section
+# 3.1 lets b_q and b_k differ; b_k is the 64-key block of the flash loop and
+# b_q = 128 query rows (two quantization blocks) share one mask row.
+SPARSE_BQ = 128
+SPARSE_BK = BLOCK
 
 
 def block_scores(q_means, k_means) -> np.ndarray:
@@ -514,8 +521,9 @@ def block_scores(q_means, k_means) -> np.ndarray:
     return np.asarray(q_means, dtype=F64) @ np.asarray(k_means, dtype=F64).T
 
 
-def sparse_block_mask(s_hat, topn: int, L: int, prefix: int, grid) -> np.ndarray:
-    """Block mask M [NB, NB] of the block-sparse flash loop (RainFusion2.0 sections 3.1, 3.2, 3.4).
+def sparse_block_mask(s_hat, topn: int, L: int, prefix: int, grid, bq: int = SPARSE_BQ,
+                      bk: int = SPARSE_BK) -> np.ndarray:
+    """Block mask M [ceil(L/bq), ceil(L/bk)] of the block-sparse flash loop (RainFusion2.0 sections 3.1, 3.2, 3.4).
 
     M[i, j] = 1 for the topn key blocks j with the largest S_hat[i, j]
     (reading of "the top-n important blocks K_j for each block Q_i"; the
@@ -525,15 +533,15 @@ def sparse_block_mask(s_hat, topn: int, L: int, prefix: int, grid) -> np.ndarray
     block that holds a sink token keeps every key block.
     """
     s_hat = np.asarray(s_hat, dtype=F64)
-    nb = s_hat.shape[0]
-    M = np.zeros((nb, nb), dtype=bool)
-    n = min(int(topn), nb)
-    for i in range(nb):
-        order = sorted(range(nb), key=lambda j: (-s_hat[i, j], j))
+    nq, nk = s_hat.shape
+    M = np.zeros((nq, nk), dtype=bool)
+    n = min(int(topn), nk)
+    for i in range(nq):
+        order = sorted(range(nk), key=lambda j: (-s_hat[i, j], j))
         M[i, order[:n]] = True
-    ns = -(-sink_end(L, prefix, grid) // BLOCK)     # blocks holding a sink token
-    M[:, :ns] = True
-    M[:ns, :] = True
+    se = sink_end(L, prefix, grid)
+    M[:, :-(-se // bk)] = True                       # key blocks holding a sink token
+    M[:-(-se // bq), :] = True                       # query blocks holding a sink token
     return M
 
 
@@ -542,20 +550,23 @@ def sparse_forward_head(q16, k16, v16, *, prefix, grid, split, base, rotation, t
     """Block-sparse INT4 attention of one head (RainFusion2.0 section 3.1: Q_i K_j^T and P_ij V_j
     are skipped where M[i, j] = 0), with the quantized loop of int4_flash_rows.
 
-    block_mask: bool [NB, NB] to use instead of the one computed from the
-    block means (the GPU tests pass the mask the GPU chose after checking it
-    against s_hat). Returns dict(out, rows, mask, s_hat, q, k, v codes).
+    Query blocks of SPARSE_BQ rows, key blocks of SPARSE_BK = 64 keys; query
+    row r uses mask row r // SPARSE_BQ. block_mask: bool [NBq, NB] to use
+    instead of the one computed from the block means (the GPU tests pass the
+    mask the GPU chose after checking it against s_hat). Returns dict(out,
+    rows, mask, s_hat, q, k, v codes).
     """
     L, D = q16.shape
     qp = qk_prologue(q16, prefix, grid, split, base, rotation)
     kp = qk_prologue(k16, prefix, grid, split, base, rotation)
     vc, sv, colsum = quantize_v(v16)
-    s_hat = block_scores(block_means(q16, prefix, grid, split, base), block_means(k16, prefix, grid, split, base))
+    s_hat = block_scores(block_means(q16, prefix, grid, split, base, SPARSE_BQ),
+                         block_means(k16, prefix, grid, split, base, SPARSE_BK))
     M = sparse_block_mask(s_hat, topn, L, prefix, grid) if block_mask is None else np.asarray(block_mask, bool)
     rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, D), dtype=F64)
-    for qb in np.unique(rows // BLOCK):
-        sel = (rows // BLOCK) == qb
+    for qb in np.unique(rows // SPARSE_BQ):
+        sel = (rows // SPARSE_BQ) == qb
         p1 = int4_flash_rows(qp["codes"], qp["scale"], kp["codes"], kp["scale"], vc, sv, colsum,
                              L, D, rows[sel], key_blocks=M[qb])
         out[sel] = p1["O_scaled"] / p1["l"][:, None]

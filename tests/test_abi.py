@@ -37,7 +37,7 @@ def test_exports_match_header():
 
 def test_version_and_strerror():
     lib = _lib()
-    assert lib.rotattn_version() == 3
+    assert lib.rotattn_version() == 4
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.rotattn_strerror(code)
 
@@ -69,6 +69,10 @@ def test_sizes_720p():
     vt = 40 * 1182 * 64 * 128 * 2   # transposed fp16 V blocks of the FP16 path
     assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img + vt
     assert Bd.workspace_bytes(p, Bd.CALL_DEBUG_DUMP) == img
+    assert Bd.workspace_bytes(p, Bd.CALL_SPARSE_ATTENTION) == img
+    # block-sparse mask: one row per 128 query rows, ceil(1182 / 32) = 37 words per row
+    assert (s.mask_rows, s.mask_words, s.mask_bytes) == (591, 37, 40 * 591 * 37 * 4)
+    assert s.bsum_bytes == 40 * 1182 * 128 * 4
     # partial buffers on top only when block routing is on
     pm = Bd.problem_from_workload(W.WORKLOADS["mixed"])
     img_m = 12 * 512 * 20480   # D' = 192: 64 x 192 + 128 x 64
@@ -127,12 +131,31 @@ def test_call_validation_before_launch():
     assert lib.rotattn_fp16_forward(C.byref(p), C.c_void_p(good), C.c_void_p(good), C.c_void_p(good),
                                     C.c_void_p(good), None, 0, stream) == -4
     # dump with a negative unit count
-    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, -1, None, None, None, None,
-                                  None, 0, stream) == -1
+    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, None, -1, None, None, None,
+                                  None, None, 0, stream) == -1
     # dump without its workspace (the K/V block images)
     one = C.c_void_p(good)
-    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, one, 1, one, one, one, one,
+    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, one, 1, one, one, one, one,
                                   None, 0, stream) == -4
+    # dump with a block mask and a head mask together
+    assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), one, one, one, 1, one, one, one, one,
+                                  None, 0, stream) == -1
+    # block mask: needs the block sums; topn < 1; null or misaligned mask (no workspace needed)
+    assert Bd.workspace_bytes(p, Bd.CALL_BLOCK_MASK) == 0
+    qks = Bd.QKBuffers(*([good] * 7 + [None, None, good, good]))
+    assert lib.rotattn_block_mask(C.byref(p), C.byref(qk), 4, one, None, 0, stream) == -1
+    assert lib.rotattn_block_mask(C.byref(p), C.byref(qks), 0, one, None, 0, stream) == -1
+    assert lib.rotattn_block_mask(C.byref(p), C.byref(qks), 4, None, None, 0, stream) == -1
+    assert lib.rotattn_block_mask(C.byref(p), C.byref(qks), 4, C.c_void_p(good + 2), None, 0, stream) == -3
+    qkm = Bd.QKBuffers(*([good] * 7 + [None, None, good + 4, good]))
+    assert lib.rotattn_block_mask(C.byref(p), C.byref(qkm), 4, one, None, 0, stream) == -3
+    # sparse attention: null mask; block routing on; no workspace
+    assert lib.rotattn_sparse_attention(C.byref(p), C.byref(qk), C.byref(vb), None, one, one, 1 << 30,
+                                        stream) == -1
+    pr = _p(block_err_tau=0.05)
+    assert lib.rotattn_sparse_attention(C.byref(pr), C.byref(qk), C.byref(vb), one, one, one, 1 << 30,
+                                        stream) == -1
+    assert lib.rotattn_sparse_attention(C.byref(p), C.byref(qk), C.byref(vb), one, one, None, 0, stream) == -4
 
 
 def test_empty_problem_is_a_no_op():

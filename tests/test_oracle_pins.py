@@ -603,22 +603,28 @@ def test_block_means_brute_force_and_tail():
             assert got[i, d] == pytest.approx(acc / (b - a), rel=1e-12, abs=1e-15)
     # the ragged block is not diluted by the 61 padded rows
     assert not np.allclose(got[1], xr[64:].astype(np.float64).sum(0) / 64, rtol=1e-3)
+    # one 128-token block (67 valid tokens) is the count-weighted mean of the two 64-token means
+    got128 = O.block_means(x, prefix, grid, split, 10000.0, 128)
+    assert got128.shape == (1, D)
+    assert np.allclose(got128[0], (64 * got[0] + 3 * got[1]) / 67, rtol=1e-12, atol=1e-15)
 
 
 def test_block_scores_are_tile_means_of_scores():
-    """S_hat[i, j] = q_hat_i . k_hat_j equals the mean of q_a . k_b over the tile (a in Q_i, b in K_j), by bilinearity."""
+    """S_hat[i, j] = q_hat_i . k_hat_j equals the mean of q_a . k_b over the 128 x 64 tile (a in Q_i, b in K_j), by bilinearity."""
     rng = _rng(32)
     L, D, prefix, grid, split = 150, 16, 0, (1, 10, 15), (6, 5, 5)
     q = rng.standard_normal((L, D)).astype(np.float16)
     k = rng.standard_normal((L, D)).astype(np.float16)
-    s_hat = O.block_scores(O.block_means(q, prefix, grid, split, 10000.0), O.block_means(k, prefix, grid, split, 10000.0))
+    bq, bk = O.SPARSE_BQ, O.SPARSE_BK
+    s_hat = O.block_scores(O.block_means(q, prefix, grid, split, 10000.0, bq),
+                           O.block_means(k, prefix, grid, split, 10000.0, bk))
     qr = O.apply_rope(q.astype(F32), prefix, grid, split, 10000.0).astype(np.float64)
     kr = O.apply_rope(k.astype(F32), prefix, grid, split, 10000.0).astype(np.float64)
     S = qr @ kr.T
-    nb = O.n_blocks(L)
-    for i in range(nb):
-        for j in range(nb):
-            tile = S[64 * i:min(L, 64 * i + 64), 64 * j:min(L, 64 * j + 64)]
+    assert s_hat.shape == (-(-L // bq), -(-L // bk)) == (2, 3)
+    for i in range(s_hat.shape[0]):
+        for j in range(s_hat.shape[1]):
+            tile = S[bq * i:min(L, bq * i + bq), bk * j:min(L, bk * j + bk)]
             assert s_hat[i, j] == pytest.approx(tile.mean(), rel=1e-10, abs=1e-12)
 
 
@@ -639,14 +645,17 @@ def test_sparse_mask_rank_count_brute_force():
     rng = _rng(34)
     nb, n = 9, 3
     s = rng.integers(-3, 4, (nb, nb)).astype(np.float64)     # many ties
-    L, prefix, grid = nb * 64, 10, (3, 10, 17)                # sink_end = 10 + 170 = 180 -> blocks 0..2
-    M = O.sparse_block_mask(s, n, L, prefix, grid)
+    L, prefix, grid = nb * 64, 10, (3, 10, 17)                # sink_end = 10 + 170 = 180 -> key blocks 0..2
+    M = O.sparse_block_mask(s, n, L, prefix, grid, bq=64)
     for i in range(nb):
         for j in range(nb):
             rank = sum(1 for kk in range(nb) if s[i, kk] > s[i, j] or (s[i, kk] == s[i, j] and kk < j))
             want = rank < n or j <= 2 or i <= 2
             assert M[i, j] == want, (i, j)
     assert M[:3].all() and M[:, :3].all()
+    # 128-row query blocks: the sink (tokens < 180) lies in query blocks 0 and 1
+    M2 = O.sparse_block_mask(s[:5], n, L, prefix, grid, bq=128)
+    assert M2[:2].all() and M2[:, :3].all() and not M2[2:, 3:].all()
 
 
 def test_sparse_mask_worked_example():
@@ -657,14 +666,14 @@ def test_sparse_mask_worked_example():
                   [9., 8., 7., 6., 5.],
                   [2., 9., 2., 9., 1.]])
     L, prefix, grid = 5 * 64, 0, (5, 8, 8)                    # frame 0 = block 0 is the sink
-    M = O.sparse_block_mask(s, 2, L, prefix, grid)
+    M = O.sparse_block_mask(s, 2, L, prefix, grid, bq=64)
     want = np.array([[1, 1, 1, 1, 1],                         # sink query block
                      [1, 0, 0, 1, 1],
                      [1, 1, 0, 0, 0],                         # all equal: lowest j
                      [1, 1, 0, 0, 0],
                      [1, 1, 0, 1, 0]], dtype=bool)
     assert np.array_equal(M, want)
-    assert O.sparse_block_mask(s, 5, L, prefix, grid).all()
+    assert O.sparse_block_mask(s, 5, L, prefix, grid, bq=64).all()
 
 
 def test_sparse_forward_dense_mask_equals_dense_path():
@@ -698,11 +707,11 @@ def test_sparse_forward_masked_softmax_identity():
 
 
 def test_sparse_sink_rows_are_dense():
-    """Query blocks that hold first-frame tokens keep every key block, so their outputs equal the dense path's."""
+    """Query blocks (128 rows) that hold first-frame tokens keep every key block, so their outputs equal the dense path's."""
     w = W.WORKLOADS["tiny"]
     x = W.head_inputs(w, 0, 0)
     kw = dict(prefix=w.prefix, grid=w.grid, split=w.split, base=w.base, rotation=w.rotation)
-    rows = np.arange(0, 64)                                   # frame 0 of the 4x8x8 grid = block 0
+    rows = np.arange(0, 128)                                  # frame 0 of the 4x8x8 grid is in query block 0
     sp = O.sparse_forward_head(x["q"], x["k"], x["v"], topn=1, rows=rows, **kw)
     dn = O.forward_head(x["q"], x["k"], x["v"], rows=rows, **kw)
     assert not sp["mask"][1:, 1:].all()
