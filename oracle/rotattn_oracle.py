@@ -11,8 +11,9 @@ What it computes, step by step, in the pages' order:
      width frequency groups). Token order is frame-major [F, H, W]
      (RainFusion2.0, section "3D Window Permutation", default layout).
   2. A Walsh-Hadamard rotation applied after RoPE to Q and K (RotateAttention
-     abstract, "RoPE-aware Rotation", the negligible-overhead online variant).
-     The rotation is orthonormal, so Q K^T is unchanged.
+     abstract, "RoPE-aware Rotation", the negligible-overhead online variant),
+     or the mergeable variant folded into RoPE (pair_phase). Either rotation
+     is orthonormal, so Q K^T is unchanged.
   3. Symmetric INT4 quantization of Q and K per 64-token block, and of V per
      channel (RotateAttention abstract: mixed-precision INT4 FlashAttention).
   4. The flash loop of RainFusion2.0 section 3.1 "Blockwise Sparse" (the
@@ -53,6 +54,7 @@ F64 = np.float64
 BLOCK = 64          # tokens per quantization block and per flash key block
 ROT_FULL = 0
 ROT_GROUP64 = 1
+ROT_PAIR = 2        # the mergeable rotation, fused into RoPE (see pair_phase)
 
 
 # --------------------------------------------------------------------------
@@ -101,11 +103,11 @@ def rope_thetas(split, base: float) -> list[list[float]]:
     return out
 
 
-def rope_tables(grid, split, base: float):
+def rope_tables(grid, split, base: float, phase: float = 0.0):
     """float32 cos/sin tables per axis: list of (cos[n_pos, npair], sin[n_pos, npair]).
 
-    Angles and their cos/sin are evaluated in float64 and rounded once to
-    float32.
+    Angles pos * theta_i + phase and their cos/sin are evaluated in float64
+    and rounded once to float32.
     """
     tabs = []
     for a, thetas in enumerate(rope_thetas(split, base)):
@@ -114,25 +116,49 @@ def rope_tables(grid, split, base: float):
         s = np.empty((n_pos, len(thetas)), dtype=F32)
         for p in range(n_pos):
             for i, th in enumerate(thetas):
-                ang = float(p) * th
+                ang = float(p) * th + phase
                 c[p, i] = F32(math.cos(ang))
                 s[p, i] = F32(math.sin(ang))
         tabs.append((c, s))
     return tabs
 
 
-def apply_rope(x32: np.ndarray, prefix: int, grid, split, base: float) -> np.ndarray:
+def pair_phase() -> float:
+    """Angle of the mergeable RoPE-aware rotation (RotateAttention abstract, "RoPE-aware Rotation").
+
+    Reading: the abstract names "mergeable rotation matrices that can be
+    fused into RoPE" without constructing them. An orthogonal R can be merged
+    into RoPE (RoPE_pos(x) R = RoPE_pos(x R) for every position, so R can be
+    folded into the Q/K projections or into RoPE's tables) exactly when it
+    commutes with every 3D-RoPE rotation; with the distinct frequencies of an
+    axis group and the independent positions of the three axes, those are the
+    matrices that turn each RoPE pair (2i, 2i+1) by a fixed angle in its own
+    plane and leave an odd group's unpaired dim alone. The angle taken here
+    is pi/4 for every pair: it spreads a pair's energy evenly over its two
+    dims, the most a within-pair rotation can flatten a one-dim outlier.
+    Folded into RoPE, every pair of a video token turns by pos * theta_i +
+    pi/4 and every pair of a text token by pi/4.
+    """
+    return math.pi / 4
+
+
+def apply_rope(x32: np.ndarray, prefix: int, grid, split, base: float, phase: float = 0.0) -> np.ndarray:
     """3D RoPE in float32: per pair y0 = x0*c - x1*s, y1 = x0*s + x1*c.
 
     Each product and each sum is rounded to float32 separately (no fused
-    multiply-add). Text tokens are returned unchanged.
+    multiply-add). With phase = 0 text tokens are returned unchanged; with a
+    phase (the mergeable rotation folded into RoPE, see pair_phase) every
+    pair of a video token turns by pos * theta_i + phase and every pair of a
+    text token by phase alone, with float32(cos phase), float32(sin phase).
     """
     assert x32.dtype == F32
     L, D = x32.shape
     assert sum(split) == D
     coords, video = token_coords(L, prefix, grid)
+    text = ~video
     y = x32.copy()
-    tabs = rope_tables(grid, split, base)
+    tabs = rope_tables(grid, split, base, phase)
+    ct, st = F32(math.cos(phase)), F32(math.sin(phase))
     for a, off in enumerate(group_offsets(split)):
         c_tab, s_tab = tabs[a]
         pos = coords[video, a]
@@ -144,6 +170,11 @@ def apply_rope(x32: np.ndarray, prefix: int, grid, split, base: float) -> np.nda
             x1 = x32[video, d1]
             y[video, d0] = (x0 * c) - (x1 * s)
             y[video, d1] = (x0 * s) + (x1 * c)
+            if phase != 0.0 and text.any():
+                t0 = x32[text, d0]
+                t1 = x32[text, d1]
+                y[text, d0] = (t0 * ct) - (t1 * st)
+                y[text, d1] = (t0 * st) + (t1 * ct)
     return y
 
 
@@ -184,6 +215,8 @@ def fwht(x32: np.ndarray) -> np.ndarray:
 def rotate(x32: np.ndarray, rotation: int, split) -> np.ndarray:
     """RoPE-aware rotation x' = x . R applied after RoPE (float32).
 
+    ROT_PAIR: the mergeable rotation; it is applied inside RoPE (see
+    pair_phase), so nothing is left to do here.
     ROT_FULL: R = H_D / sqrt(D) over the whole head dim.
     ROT_GROUP64 (reading of "block-diagonal Hadamard per RoPE group, 44 -> pad
     64, 42 -> pad 64"): each RoPE group is zero padded to 64 dims and turned
@@ -191,6 +224,8 @@ def rotate(x32: np.ndarray, rotation: int, split) -> np.ndarray:
     is 192. The kept rows of an orthonormal matrix are orthonormal, so
     x' y'^T = x y^T.
     """
+    if rotation == ROT_PAIR:   # already folded into RoPE (apply_rope with pair_phase)
+        return x32
     if rotation == ROT_FULL:
         return fwht(x32)
     if rotation == ROT_GROUP64:
@@ -579,9 +614,13 @@ def sparse_forward_head(q16, k16, v16, *, prefix, grid, split, base, rotation, t
 # --------------------------------------------------------------------------
 
 def qk_prologue(x16, prefix, grid, split, base, rotation):
-    """RoPE, rotation and block quantization of one Q or K head [L, D] float16."""
+    """RoPE, rotation and block quantization of one Q or K head [L, D] float16.
+
+    With ROT_PAIR the rotation is folded into RoPE, so "rope32"/"rope16" (the
+    FP16 path's inputs) are the rotated vectors; Q K^T is the same either way.
+    """
     x32 = x16.astype(F32)
-    xr = apply_rope(x32, prefix, grid, split, base)
+    xr = apply_rope(x32, prefix, grid, split, base, pair_phase() if rotation == ROT_PAIR else 0.0)
     xrot = rotate(xr, rotation, split)
     codes, scales, nsr = quantize_qk_blocks(xrot)
     return {"rope32": xr, "rope16": xr.astype(np.float16), "rot": xrot,

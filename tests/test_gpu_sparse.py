@@ -185,3 +185,38 @@ def test_sparse_custom_mask_edges(sel):
                                   rows=rows)
         err = np.abs(out[0, h, rows] - o["out"])
         assert (err <= G.ATOL + G.RTOL * np.abs(o["out"])).all(), float(err.max())
+
+
+def test_sparse_strided_batch():
+    """B = 2 with tokens-major [B, L, H, D] storage, D = 64, a text prefix and a ragged last block: the mask and
+    every output row against the oracle (run with the GPU's mask after checking it)."""
+    G.require_gpu()
+    w = W.WORKLOADS["smalld"].replace(B=2, H=3, grid=(3, 10, 20), prefix=9)     # L = 609, NB = 10, 5 mask rows
+    x = W.full_inputs(w)
+    B, H, L, D = w.B, w.H, w.L, w.D
+    topn = 2
+
+    def put(a):
+        return torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).cuda().permute(0, 2, 1, 3)
+    p = G.R.problem_from_workload(w, strides=(L * H * D, D, H * D))
+    s = G.R.get_sizes(p)
+    q, k, v = put(x["q"]), put(x["k"]), put(x["v"])
+    out = torch.empty((B, L, H, D), dtype=torch.float16, device="cuda").permute(0, 2, 1, 3)
+    qk = G.R.rotattn_quantize_qk(p, q, k, block_sums=True)
+    vq = G.R.rotattn_quantize_v(p, v)
+    mask = G.R.rotattn_block_mask(p, qk, topn)
+    G.R.rotattn_sparse_attention(p, qk, vq, mask, out=out)
+    gm = G.R.mask_to_bool(G.host(mask).astype(np.uint32), s.NB)
+    got = G.host(out).astype(np.float64)
+    nsr, ns = _sinks(w)
+    assert (nsr, ns) == (2, 4)
+    for b in range(B):
+        for h in range(H):
+            s_hat = O.block_scores(O.block_means(x["q"][b, h], w.prefix, w.grid, w.split, w.base, O.SPARSE_BQ),
+                                   O.block_means(x["k"][b, h], w.prefix, w.grid, w.split, w.base, O.SPARSE_BK))
+            _check_mask(gm[b, h], s_hat, topn, nsr, ns)
+            o = O.sparse_forward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], prefix=w.prefix, grid=w.grid,
+                                      split=w.split, base=w.base, rotation=w.rotation, topn=topn,
+                                      block_mask=gm[b, h])
+            err = np.abs(got[b, h] - o["out"])
+            assert (err <= G.ATOL + G.RTOL * np.abs(o["out"])).all(), (b, h, float(err.max()))

@@ -716,3 +716,75 @@ def test_sparse_sink_rows_are_dense():
     dn = O.forward_head(x["q"], x["k"], x["v"], rows=rows, **kw)
     assert not sp["mask"][1:, 1:].all()
     assert np.array_equal(sp["out"], dn["out"])
+
+
+# --------------------------------------------------------------------------
+# the mergeable RoPE-aware rotation (RotateAttention abstract)
+# --------------------------------------------------------------------------
+
+def _pair_matrix(split, phase):
+    """Dense D x D per-pair plane rotation by `phase` (row-vector convention), identity on unpaired dims."""
+    D = sum(split)
+    R = np.eye(D)
+    c, s = math.cos(phase), math.sin(phase)
+    off = 0
+    for g in split:
+        for i in range(g // 2):
+            d0, d1 = off + 2 * i, off + 2 * i + 1
+            R[d0, d0], R[d1, d0], R[d0, d1], R[d1, d1] = c, -s, s, c
+        off += g
+    return R
+
+
+@pytest.mark.parametrize("split", [(44, 42, 42), (22, 21, 21)])
+def test_pair_rotation_commutes_with_rope(split):
+    """The per-pair rotation commutes with every 3D-RoPE rotation (so it can be merged into RoPE), is orthogonal,
+    and a Hadamard mixing of pairs does not commute (the reason the Hadamard variant runs after RoPE)."""
+    R = _pair_matrix(split, O.pair_phase())
+    D = sum(split)
+    assert np.allclose(R @ R.T, np.eye(D), atol=1e-14)
+    rng = _rng(41)
+    for _ in range(5):
+        coord = rng.integers(0, 50, 3)
+        M = BF.rope_matrix(coord, split, 10000.0)
+        assert np.allclose(M @ R, R @ M, atol=1e-12)
+    if D == 128:
+        H = BF.sylvester(D) / math.sqrt(D)
+        M = BF.rope_matrix((3, 5, 7), split, 10000.0)
+        assert not np.allclose(M @ H, H @ M, atol=1e-3)
+
+
+@pytest.mark.parametrize("split,prefix", [((44, 42, 42), 0), ((22, 21, 21), 5)])
+def test_pair_rotation_folded_equals_rope_then_rotation(split, prefix):
+    """RoPE with the phase folded into its angles equals the dense RoPE matrix followed by the dense pair rotation
+    (text tokens: the pair rotation alone), to float32 rounding."""
+    rng = _rng(42)
+    grid = (2, 3, 4)
+    D = sum(split)
+    L = prefix + 24
+    x = rng.standard_normal((L, D)).astype(np.float32)
+    got = O.apply_rope(x, prefix, grid, split, 10000.0, O.pair_phase()).astype(np.float64)
+    R = _pair_matrix(split, O.pair_phase())
+    for n in range(L):
+        c = BF.coords_of(n, prefix, grid)
+        M = np.eye(D) if c is None else BF.rope_matrix(c, split, 10000.0)
+        want = x[n].astype(np.float64) @ M @ R
+        assert np.allclose(got[n], want, rtol=0, atol=4e-6 * (1 + np.abs(want).max())), n
+
+
+def test_pair_rotation_preserves_qk_and_spreads_outliers():
+    """Q' K'^T equals RoPE(Q) RoPE(K)^T; a pair whose energy sits in one dim is split evenly over both."""
+    rng = _rng(43)
+    grid, split = (1, 4, 8), (44, 42, 42)
+    q = rng.standard_normal((32, 128)).astype(np.float32)
+    k = rng.standard_normal((32, 128)).astype(np.float32)
+    a = O.apply_rope(q, 0, grid, split, 10000.0, O.pair_phase()).astype(np.float64)
+    b = O.apply_rope(k, 0, grid, split, 10000.0, O.pair_phase()).astype(np.float64)
+    qr = O.apply_rope(q, 0, grid, split, 10000.0).astype(np.float64)
+    kr = O.apply_rope(k, 0, grid, split, 10000.0).astype(np.float64)
+    assert np.allclose(a @ b.T, qr @ kr.T, rtol=1e-5, atol=1e-4)
+    # text token with (x0, x1) = (1, 0) in every pair: both dims become 1/sqrt(2)
+    e = np.zeros((1, 128), np.float32)
+    e[0, 0::2] = 1.0
+    y = O.apply_rope(e, 1, (0, 0, 0), split, 10000.0, O.pair_phase())
+    assert np.allclose(np.abs(y[0]), 1 / math.sqrt(2), atol=1e-7)

@@ -28,6 +28,7 @@ import numpy as np
 
 ROT_FULL = 0       # one Walsh-Hadamard over the whole head dim
 ROT_GROUP64 = 1    # one 64-point Walsh-Hadamard per RoPE group, zero padded
+ROT_PAIR = 2       # the mergeable rotation: every RoPE pair turned by pi/4, folded into RoPE
 
 _TENSOR_ID = {"q": 0, "k": 1, "v": 2}
 
@@ -41,7 +42,7 @@ class Workload:
     grid: tuple            # (T, Hh, W) latent token grid
     prefix: int            # text tokens placed before the video tokens (no RoPE)
     split: tuple           # RoPE dims for the (t, h, w) axes, contiguous, in that order
-    rotation: int          # ROT_FULL or ROT_GROUP64
+    rotation: int          # ROT_FULL, ROT_GROUP64 or ROT_PAIR
     std: float             # standard deviation of the Gaussian body
     outliers: str          # "group_const", "t3", "lognormal"
     outlier_factor: float  # multiplier for "group_const"
