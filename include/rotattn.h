@@ -30,7 +30,8 @@
  * text prefix (no RoPE) followed by the video latent grid grid_t x grid_h x
  * grid_w flattened frame-major, the default [F, H, W] order of RainFusion2.0
  * ("3D Window Permutation"). Lp = L rounded up to a multiple of 64,
- * NB = Lp / 64, D' = D for ROTATTN_ROT_FULL and 192 for ROTATTN_ROT_GROUP64.
+ * NB = Lp / 64, D' = D for ROTATTN_ROT_FULL and ROTATTN_ROT_PAIR, 192 for
+ * ROTATTN_ROT_GROUP64.
  */
 #ifndef ROTATTN_H
 #define ROTATTN_H
@@ -55,6 +56,9 @@ extern "C" {
 /* rotation applied after RoPE (RotateAttention abstract, "RoPE-aware Rotation") */
 #define ROTATTN_ROT_FULL    0  /* x' = x H_D / sqrt(D) over the whole head dim; D' = D */
 #define ROTATTN_ROT_GROUP64 1  /* each RoPE group zero padded to 64 and turned by H_64 / 8; D' = 192 */
+#define ROTATTN_ROT_PAIR    2  /* the mergeable rotation: every RoPE pair (2i, 2i+1) turned by pi/4 in its own
+                                  plane, folded into RoPE (video tokens: angle pos * theta_i + pi/4; text tokens:
+                                  pi/4); it commutes with every RoPE rotation; D' = D */
 
 /* calls, for rotattn_workspace_bytes */
 #define ROTATTN_CALL_QUANTIZE_QK 0
@@ -74,7 +78,7 @@ typedef struct rotattn_problem {
   int32_t grid_t, grid_h, grid_w;  /* video latent grid; L = text_prefix + grid_t*grid_h*grid_w */
   int32_t text_prefix;             /* leading text tokens that take no RoPE */
   int32_t rope_split[3];           /* head dims of the t, h, w RoPE groups, contiguous, sum = D */
-  int32_t rotation;                /* ROTATTN_ROT_FULL or ROTATTN_ROT_GROUP64 */
+  int32_t rotation;                /* ROTATTN_ROT_FULL, ROTATTN_ROT_GROUP64 or ROTATTN_ROT_PAIR */
   double rope_base;                /* RoPE frequency base (10000) */
   int64_t stride_b, stride_h, stride_l; /* element strides of q, k, v and out; the D axis is contiguous */
   float block_err_tau;             /* a Q/K block whose quantization NSR exceeds this runs on FP16; +inf: never */
@@ -90,7 +94,8 @@ typedef struct rotattn_qk_buffers {
   uint8_t* q_flag;      /* [B][H][NB] 1 if the block's quantization NSR > block_err_tau */
   uint8_t* k_flag;
   uint32_t* head_kflag; /* [B*H] nonzero if any K block of the head is flagged */
-  void* q_rope;         /* optional fp16 [B][H][L][D] (dense): RoPE'd, unrotated Q for the FP16 path; NULL = not written */
+  void* q_rope;         /* optional fp16 [B][H][L][D] (dense): RoPE'd, unrotated Q for the FP16 path (with
+                           ROTATTN_ROT_PAIR the pair rotation is part of RoPE and included); NULL = not written */
   void* k_rope;         /* optional, as q_rope */
   float* q_bsum;        /* optional float [B][H][NB][D] (16-byte aligned): per 64-token block, the sum of the RoPE'd,
                            unrotated rows over the block's valid tokens (float32, ascending token order); the input
@@ -138,8 +143,9 @@ int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes);
 
 /*
  * Steps 1-3 for Q and K (RotateAttention abstract): 3D RoPE (float32, each
- * pair turned by pos * base^(-2i/g_rot) of its axis group), the
- * Walsh-Hadamard rotation, symmetric INT4 quantization per 64-token block
+ * pair turned by pos * base^(-2i/g_rot) of its axis group), the RoPE-aware
+ * rotation (the Walsh-Hadamard after RoPE, or with ROTATTN_ROT_PAIR the pair
+ * rotation folded into RoPE), symmetric INT4 quantization per 64-token block
  * (s = absmax/7, codes clamp(rne(x/s), -7, 7)) and the block error flags
  * (NSR = |x - s c|^2 / |x|^2 > block_err_tau); optionally the RoPE'd block
  * sums of block-sparse attention (out->q_bsum, out->k_bsum).

@@ -6,12 +6,12 @@ librotattn.so has not been built.
 """
 from . import binding  # noqa: F401
 from .binding import (  # noqa: F401
-    ROT_FULL, ROT_GROUP64, Problem, QKCodes, VCodes, RotattnError, make_problem, problem_from_workload,
+    ROT_FULL, ROT_GROUP64, ROT_PAIR, Problem, QKCodes, VCodes, RotattnError, make_problem, problem_from_workload,
     get_sizes, workspace_bytes, rotattn_quantize_qk, rotattn_quantize_v, rotattn_attention, rotattn_forward,
     rotattn_fp16_forward, rotattn_debug_dump, rotattn_block_mask, rotattn_sparse_attention, mask_to_bool,
     load_library,
 )
 
 __all__ = [n for n in dir() if n.startswith("rotattn_") or n in (
-    "ROT_FULL", "ROT_GROUP64", "Problem", "QKCodes", "VCodes", "RotattnError", "make_problem",
+    "ROT_FULL", "ROT_GROUP64", "ROT_PAIR", "Problem", "QKCodes", "VCodes", "RotattnError", "make_problem",
     "problem_from_workload", "get_sizes", "workspace_bytes", "load_library")]

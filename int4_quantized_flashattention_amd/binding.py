@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "librotattn.so")
 
 ROT_FULL = 0
 ROT_GROUP64 = 1
+ROT_PAIR = 2
 
 CALL_QUANTIZE_QK = 0
 CALL_QUANTIZE_V = 1

@@ -28,6 +28,10 @@ struct KProblem {
   double base;
   int tab_off[3];            // float offset of each axis's cos table; sin follows after n_pos*npair floats
   int tab_floats;            // total floats of all tables
+  // the mergeable rotation (rotation 2): a fixed angle added to every RoPE
+  // pair's angle, and its float cos/sin for the pairs of text tokens
+  double pair_phase;
+  float pair_c, pair_s;
 };
 
 __device__ __forceinline__ float fmul_rn(float a, float b) { return __fmul_rn(a, b); }
@@ -179,7 +183,8 @@ struct AttnArgs {
   int32_t* d_acc; int8_t* d_pq; int32_t* d_pv; float* d_m;
 };
 
-hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, hipStream_t s);
+hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, double phase,
+                              hipStream_t s);
 hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half* k, const float* tab,
                               const QKOut& o, hipStream_t s);
 hipError_t launch_rope_copy(const KProblem& kp, const __half* x, const float* tab, __half* dst, hipStream_t s);

@@ -21,10 +21,11 @@
 
 namespace rotattn {
 
-// cos/sin of every (axis, position, pair): angle = pos * base^(-2i / g_rot),
-// evaluated in double and rounded once to float. Also zeroes a small u32
-// array (the per-head flag summary) so that one launch prepares both.
-__global__ void rope_table_kernel(KProblem kp, float* tab, uint32_t* zero_u32, int n_zero) {
+// cos/sin of every (axis, position, pair): angle = pos * base^(-2i / g_rot)
+// + phase (phase: the mergeable rotation folded into RoPE, else 0), evaluated
+// in double and rounded once to float. Also zeroes a small u32 array (the
+// per-head flag summary) so that one launch prepares both.
+__global__ void rope_table_kernel(KProblem kp, float* tab, uint32_t* zero_u32, int n_zero, double phase) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (zero_u32 != nullptr && i < n_zero) zero_u32[i] = 0u;
   int rem = i;
@@ -35,7 +36,7 @@ __global__ void rope_table_kernel(KProblem kp, float* tab, uint32_t* zero_u32, i
     if (rem < n) {
       const int p = rem / np, pi = rem - (rem / np) * np;
       const double th = pow(kp.base, -(2.0 * pi) / (double)(2 * np));
-      const double ang = (double)p * th;
+      const double ang = (double)p * th + phase;
       tab[kp.tab_off[a] + rem] = (float)cos(ang);
       tab[kp.tab_off[a] + n + rem] = (float)sin(ang);
       return;
@@ -69,8 +70,10 @@ __device__ __forceinline__ void load_block_to_lds(const KProblem& kp, const __ha
   for (int e = 0; e < PER; ++e) Y[tok][part * PER + e] = vals[e];
 }
 
-// RoPE in place on the LDS tile: one task per (token, pair).
-template <int D>
+// RoPE in place on the LDS tile: one task per (token, pair). With PAIR the
+// mergeable rotation is folded in: the tables carry the extra angle and the
+// pairs of text tokens turn by it alone.
+template <int D, bool PAIR = false>
 __device__ __forceinline__ void rope_lds(const KProblem& kp, const float* tab, int blk, float (*Y)[D + 4]) {
   const int npt = kp.npair[0] + kp.npair[1] + kp.npair[2];
   const int n0 = kp.T * kp.npair[0], n1 = kp.Hh * kp.npair[1], n2 = kp.W * kp.npair[2];
@@ -78,7 +81,19 @@ __device__ __forceinline__ void rope_lds(const KProblem& kp, const float* tab, i
     const int tok = task / npt;
     int pr = task - tok * npt;
     const int tg = blk * kBlock + tok;
-    if (tg >= kp.L || tg < kp.prefix) continue;
+    if (tg >= kp.L) continue;
+    if (tg < kp.prefix) {
+      if (PAIR) {
+        int a = 0;
+        if (pr >= kp.npair[0]) { pr -= kp.npair[0]; a = 1; }
+        if (a == 1 && pr >= kp.npair[1]) { pr -= kp.npair[1]; a = 2; }
+        const int d0 = kp.off[a] + 2 * pr;
+        const float x0 = Y[tok][d0], x1 = Y[tok][d0 + 1];
+        Y[tok][d0] = fsub_rn(fmul_rn(x0, kp.pair_c), fmul_rn(x1, kp.pair_s));
+        Y[tok][d0 + 1] = fadd_rn(fmul_rn(x0, kp.pair_s), fmul_rn(x1, kp.pair_c));
+      }
+      continue;
+    }
     const int idx = tg - kp.prefix;
     int a, pos, nA;
     if (pr < kp.npair[0]) {
@@ -139,7 +154,7 @@ template <int D, int ROT>
 __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __half* q, const __half* k,
                                                           const float* tab, QKOut o) {
   constexpr int DP = (ROT == 1) ? 192 : D;
-  constexpr int N = (ROT == 1) ? 64 : D;       // Walsh-Hadamard size
+  constexpr int N = (ROT == 1) ? 64 : D;       // Walsh-Hadamard size (ROT 2: no Hadamard)
   constexpr int PARTS = DP / 32;               // 32-value chunks per token
   constexpr int TASKS = kBlock * PARTS;        // multiple of 64
   constexpr int ROUNDS = (TASKS + 255) / 256;
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
 
   load_block_to_lds<D>(kp, x, b, h, blk, Y);
   __syncthreads();
-  rope_lds<D>(kp, tab, blk, Y);
+  rope_lds<D, ROT == 2>(kp, tab, blk, Y);
   __syncthreads();
   __half* rcopy = tensor ? o.k_rope : o.q_rope;
   if (rcopy != nullptr) store_rope_copy<D>(kp, b, h, blk, Y, rcopy);
@@ -188,6 +203,7 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
           v[r][e] = Y[tok][p];
         }
       }
+      if constexpr (ROT != 2) {
 #pragma unroll
       for (int hs = 1; hs < 32; hs <<= 1) {
 #pragma unroll
@@ -211,10 +227,10 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
       }
       const float rn = (N == 128) ? 0.08838834764831845f : (N == 64) ? 0.125f : 0.f;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        v[r][j] = fmul_rn(v[r][j], rn);
-        amax = fmaxf(amax, fabsf(v[r][j]));
-      }
+      for (int j = 0; j < 32; ++j) v[r][j] = fmul_rn(v[r][j], rn);
+      }   // ROT != 2
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[r][j]));
     }
   }
   amax = block_reduce_max(amax, red);
@@ -269,12 +285,13 @@ __global__ __launch_bounds__(256) void rope_copy_kernel(KProblem kp, const __hal
 }
 
 
-hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, hipStream_t s) {
+hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, double phase,
+                              hipStream_t s) {
   int entries = 0;
   entries += kp.T * kp.npair[0] + kp.Hh * kp.npair[1] + kp.W * kp.npair[2];
   const int n = entries > n_zero ? entries : n_zero;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, kp, tab, zero_u32, n_zero);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, kp, tab, zero_u32, n_zero, phase);
   return hipGetLastError();
 }
 
@@ -289,6 +306,10 @@ hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half*
     hipLaunchKernelGGL((qk_prologue_kernel<64, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
   else if (kp.D == 64 && kp.rotation == 1)
     hipLaunchKernelGGL((qk_prologue_kernel<64, 1>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+  else if (kp.D == 128 && kp.rotation == 2)
+    hipLaunchKernelGGL((qk_prologue_kernel<128, 2>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+  else if (kp.D == 64 && kp.rotation == 2)
+    hipLaunchKernelGGL((qk_prologue_kernel<64, 2>), grid, dim3(256), 0, s, kp, q, k, tab, o);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

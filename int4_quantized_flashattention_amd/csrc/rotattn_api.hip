@@ -29,7 +29,8 @@ int derive(const rotattn_problem* p, Derived* d) {
   if (p->B < 1 || p->H < 1 || p->L < 0 || p->text_prefix < 0) return ROTATTN_EINVAL;
   if (p->grid_t < 0 || p->grid_h < 0 || p->grid_w < 0) return ROTATTN_EINVAL;
   if (p->D != 64 && p->D != 128) return ROTATTN_EUNSUPPORTED;
-  if (p->rotation != ROTATTN_ROT_FULL && p->rotation != ROTATTN_ROT_GROUP64) return ROTATTN_EINVAL;
+  if (p->rotation != ROTATTN_ROT_FULL && p->rotation != ROTATTN_ROT_GROUP64 && p->rotation != ROTATTN_ROT_PAIR)
+    return ROTATTN_EINVAL;
   const int64_t video = (int64_t)p->grid_t * p->grid_h * p->grid_w;
   if ((int64_t)p->text_prefix + video != (int64_t)p->L) return ROTATTN_EINVAL;
   if (p->L > (1 << 30)) return ROTATTN_EUNSUPPORTED;
@@ -67,6 +68,10 @@ int derive(const rotattn_problem* p, Derived* d) {
   }
   k.tab_floats = toff;
   k.rotation = p->rotation;
+  // the mergeable rotation: every RoPE pair turned by pi/4 (folded into RoPE)
+  k.pair_phase = (p->rotation == ROTATTN_ROT_PAIR) ? 3.14159265358979323846 / 4.0 : 0.0;
+  k.pair_c = (float)std::cos(k.pair_phase);
+  k.pair_s = (float)std::sin(k.pair_phase);
   k.sb = p->stride_b; k.sh = p->stride_h; k.sl = p->stride_l;
   k.tau = p->block_err_tau;
   k.base = p->rope_base;
@@ -269,7 +274,7 @@ int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k, 
   if (p->L == 0) return ROTATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* tab = at<float>(workspace, L.tab);
-  rc = launched(launch_rope_tables(d.kp, tab, out->head_kflag, p->B * p->H, s));
+  rc = launched(launch_rope_tables(d.kp, tab, out->head_kflag, p->B * p->H, d.kp.pair_phase, s));
   if (rc != ROTATTN_OK) return rc;
   QKOut o;
   o.q_codes = out->q_codes; o.k_codes = out->k_codes;
@@ -353,7 +358,7 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
   float* tab = at<float>(workspace, L.tab);
   __half* qr = at<__half>(workspace, L.qr);
   __half* kr = at<__half>(workspace, L.kr);
-  if ((rc = launched(launch_rope_tables(d.kp, tab, nullptr, 0, s))) != ROTATTN_OK) return rc;
+  if ((rc = launched(launch_rope_tables(d.kp, tab, nullptr, 0, 0.0, s))) != ROTATTN_OK) return rc;   // plain RoPE
   if ((rc = launched(launch_rope_copy(d.kp, static_cast<const __half*>(q), tab, qr, s))) != ROTATTN_OK) return rc;
   if ((rc = launched(launch_rope_copy(d.kp, static_cast<const __half*>(k), tab, kr, s))) != ROTATTN_OK) return rc;
   AttnArgs a;

@@ -28,6 +28,9 @@ CASES = {
     "d64_group64": W.WORKLOADS["smalld"].replace(H=2, grid=(1, 3, 30), prefix=5, rotation=W.ROT_GROUP64),
     "lognormal": W.WORKLOADS["720p"].replace(H=2, grid=(3, 9, 16)),
     "mixed": W.WORKLOADS["mixed"].replace(H=4, grid=(2, 9, 20)),
+    "pair": W.WORKLOADS["tiny"].replace(rotation=W.ROT_PAIR),
+    "d64_pair_prefix": W.WORKLOADS["smalld"].replace(H=2, grid=(2, 5, 11), prefix=37, rotation=W.ROT_PAIR),
+    "pair_mixed": W.WORKLOADS["mixed"].replace(H=4, grid=(2, 9, 20), rotation=W.ROT_PAIR),
 }
 
 _cache = {}
