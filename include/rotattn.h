@@ -48,7 +48,8 @@ extern "C" {
 /* error codes */
 #define ROTATTN_OK            0
 #define ROTATTN_EINVAL       -1  /* null pointer, bad size, split or stride */
-#define ROTATTN_EUNSUPPORTED -2  /* head dim other than 64 or 128; a RoPE group wider than 64 with ROT_GROUP64 */
+#define ROTATTN_EUNSUPPORTED -2  /* head dim other than 64 or 128; a RoPE group wider than 64 with ROT_GROUP64;
+                                    L > 2^30, H > 65535, 2B > 65535 or B*H*NB >= 2^24 (launch limits) */
 #define ROTATTN_EALIGN       -3  /* a pointer or row stride not 16-byte aligned */
 #define ROTATTN_EWORKSPACE   -4  /* workspace missing or smaller than rotattn_workspace_bytes */
 #define ROTATTN_ELAUNCH      -5  /* a kernel launch failed */

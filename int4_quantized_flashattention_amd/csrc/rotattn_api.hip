@@ -34,6 +34,11 @@ int derive(const rotattn_problem* p, Derived* d) {
   const int64_t video = (int64_t)p->grid_t * p->grid_h * p->grid_w;
   if ((int64_t)p->text_prefix + video != (int64_t)p->L) return ROTATTN_EINVAL;
   if (p->L > (1 << 30)) return ROTATTN_EUNSUPPORTED;
+  // launch limits: a dispatch counts work-items in 32 bits per grid dimension,
+  // and the per-(head, block) launches put B*H*NB workgroups of 256 on x
+  if (p->H > 65535 || 2 * (int64_t)p->B > 65535) return ROTATTN_EUNSUPPORTED;
+  if ((int64_t)p->B * p->H * (((int64_t)p->L + kBlock - 1) / kBlock) * 256 >= (int64_t(1) << 32))
+    return ROTATTN_EUNSUPPORTED;
   int sum = 0;
   for (int a = 0; a < 3; ++a) {
     if (p->rope_split[a] < 0) return ROTATTN_EINVAL;
@@ -219,7 +224,9 @@ const char* rotattn_strerror(int code) {
   switch (code) {
     case ROTATTN_OK: return "success";
     case ROTATTN_EINVAL: return "invalid argument (null pointer, size, split, grid or stride)";
-    case ROTATTN_EUNSUPPORTED: return "unsupported problem (head dim must be 64 or 128; RoPE groups <= 64 for ROT_GROUP64)";
+    case ROTATTN_EUNSUPPORTED:
+      return "unsupported problem (head dim must be 64 or 128; RoPE groups <= 64 for ROT_GROUP64; L <= 2^30, "
+             "H <= 65535, 2B <= 65535, B*H*ceil(L/64) < 2^24)";
     case ROTATTN_EALIGN: return "pointer or row stride not 16-byte aligned (workspace: 256-byte)";
     case ROTATTN_EWORKSPACE: return "workspace missing or too small";
     case ROTATTN_ELAUNCH: return "kernel launch failed";

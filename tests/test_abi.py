@@ -91,6 +91,9 @@ def test_sizes_720p():
     (dict(rope_base=-1.0), -1),
     (dict(block_err_tau=float("nan")), -1),
     (dict(rotation=1, rope_split=(100, 14, 14)), -2),
+    (dict(H=70000), -2),                   # grid y limit
+    (dict(B=40000), -2),                   # grid z limit (two tensors per batch)
+    (dict(B=1000, H=5000), -2),            # B*H*NB = 2e7 workgroups of 256 on one grid axis
 ])
 def test_problem_validation(kw, code):
     _lib()
