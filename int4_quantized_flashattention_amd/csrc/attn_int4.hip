@@ -186,15 +186,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     h = bh0 - b * kp.H;
     row_base = qb * kBlock;
   } else {
-    // 1D grid. Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-    // contiguous run of (b, h, row tile) so that one head's K/V stream stays in
-    // one XCD's L2 instead of being fetched by all eight.
+    // 1D grid over (b, h, 128-row tile); workgroups are dealt round-robin to
+    // the 8 XCDs. Without FP16 routing each XCD gets a contiguous run of
+    // (b, h, tile), so one head's K/V stream stays in one XCD's L2 (6% faster
+    // on block-sparse problems, neutral on dense ones). With routing, whole
+    // heads may have no INT4 work: the plain order spreads every head over all
+    // XCDs so that none idles (18% faster on the mixed-precision workload).
     const int ntiles = (L + 32 * NW - 1) / (32 * NW);
-    const int total = kp.B * kp.H * ntiles;
     const int bid = blockIdx.x;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int per = total >> 3, extra = total & 7;   // XCD x gets per + (x < extra) items
-    const int logical = xcd * per + min(xcd, extra) + slot;
+    int logical = bid;
+    if (!(a.route || a.head_mask != nullptr)) {
+      const int total = kp.B * kp.H * ntiles;
+      const int xcd = bid & 7, slot = bid >> 3;
+      const int per = total >> 3, extra = total & 7;   // XCD x gets per + (x < extra) items
+      logical = xcd * per + min(xcd, extra) + slot;
+    }
     const int bhl = logical / ntiles;
     b = bhl / kp.H;
     h = bhl - b * kp.H;
