@@ -70,42 +70,55 @@ __device__ __forceinline__ void load_block_to_lds(const KProblem& kp, const __ha
   for (int e = 0; e < PER; ++e) Y[tok][part * PER + e] = vals[e];
 }
 
-// RoPE in place on the LDS tile: one task per (token, pair). With PAIR the
+// RoPE in place on the LDS tile (call after the tile's loads, with the whole
+// workgroup; it synchronizes before reading the tile and the caller
+// synchronizes after it). Thread t owns pair t % 64 (of the npair[0] +
+// npair[1] + npair[2] pairs) for the tokens t / 64 + 4 i; the video
+// coordinates of the block's tokens are computed once into `coord`. With PAIR the
 // mergeable rotation is folded in: the tables carry the extra angle and the
 // pairs of text tokens turn by it alone.
 template <int D, bool PAIR = false>
-__device__ __forceinline__ void rope_lds(const KProblem& kp, const float* tab, int blk, float (*Y)[D + 4]) {
+__device__ __forceinline__ void rope_lds(const KProblem& kp, const float* tab, int blk, float (*Y)[D + 4],
+                                         int (*coord)[3]) {
+  const int tid = threadIdx.x;
+  {
+    __syncthreads();   // the tile is loaded; coord may be rewritten
+    if (tid < kBlock) {
+      const int idx = blk * kBlock + tid - kp.prefix;
+      const int hw = kp.Hh * kp.W;
+      const int t = idx >= 0 && hw > 0 ? idx / hw : 0;
+      const int rem = idx >= 0 && hw > 0 ? idx - t * hw : 0;
+      const int hq = kp.W > 0 ? rem / kp.W : 0;
+      coord[tid][0] = t;
+      coord[tid][1] = hq;
+      coord[tid][2] = rem - hq * kp.W;
+    }
+    __syncthreads();
+  }
   const int npt = kp.npair[0] + kp.npair[1] + kp.npair[2];
-  const int n0 = kp.T * kp.npair[0], n1 = kp.Hh * kp.npair[1], n2 = kp.W * kp.npair[2];
-  for (int task = threadIdx.x; task < kBlock * npt; task += blockDim.x) {
-    const int tok = task / npt;
-    int pr = task - tok * npt;
+  int pr = tid & 63;
+  if (pr >= npt) return;   // D = 64: 31 pairs
+  int a = 0;
+  if (pr >= kp.npair[0]) { pr -= kp.npair[0]; a = 1; }
+  if (a == 1 && pr >= kp.npair[1]) { pr -= kp.npair[1]; a = 2; }
+  const int d0 = kp.off[a] + 2 * pr;
+  const int npos = (a == 0) ? kp.T : (a == 1) ? kp.Hh : kp.W;
+  const float* ctab = tab + kp.tab_off[a] + pr;
+  const float* stab = ctab + npos * kp.npair[a];
+  const int stride = kp.npair[a];
+  for (int tok = tid >> 6; tok < kBlock; tok += 4) {
     const int tg = blk * kBlock + tok;
-    if (tg >= kp.L) continue;
+    if (tg >= kp.L) break;
+    float c, s;
     if (tg < kp.prefix) {
-      if (PAIR) {
-        int a = 0;
-        if (pr >= kp.npair[0]) { pr -= kp.npair[0]; a = 1; }
-        if (a == 1 && pr >= kp.npair[1]) { pr -= kp.npair[1]; a = 2; }
-        const int d0 = kp.off[a] + 2 * pr;
-        const float x0 = Y[tok][d0], x1 = Y[tok][d0 + 1];
-        Y[tok][d0] = fsub_rn(fmul_rn(x0, kp.pair_c), fmul_rn(x1, kp.pair_s));
-        Y[tok][d0 + 1] = fadd_rn(fmul_rn(x0, kp.pair_s), fmul_rn(x1, kp.pair_c));
-      }
-      continue;
-    }
-    const int idx = tg - kp.prefix;
-    int a, pos, nA;
-    if (pr < kp.npair[0]) {
-      a = 0; pos = idx / (kp.Hh * kp.W); nA = n0;
-    } else if (pr < kp.npair[0] + kp.npair[1]) {
-      a = 1; pr -= kp.npair[0]; pos = (idx / kp.W) % kp.Hh; nA = n1;
+      if (!PAIR) continue;
+      c = kp.pair_c;
+      s = kp.pair_s;
     } else {
-      a = 2; pr -= kp.npair[0] + kp.npair[1]; pos = idx % kp.W; nA = n2;
+      const int pos = coord[tok][a];
+      c = ctab[pos * stride];
+      s = stab[pos * stride];
     }
-    const float c = tab[kp.tab_off[a] + pos * kp.npair[a] + pr];
-    const float s = tab[kp.tab_off[a] + nA + pos * kp.npair[a] + pr];
-    const int d0 = kp.off[a] + 2 * pr;
     const float x0 = Y[tok][d0], x1 = Y[tok][d0 + 1];
     Y[tok][d0] = fsub_rn(fmul_rn(x0, c), fmul_rn(x1, s));
     Y[tok][d0 + 1] = fadd_rn(fmul_rn(x0, s), fmul_rn(x1, c));
@@ -160,14 +173,14 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
   constexpr int ROUNDS = (TASKS + 255) / 256;
   __shared__ float Y[kBlock][D + 4];
   __shared__ float red[4];
+  __shared__ int coord[kBlock][3];
 
   const int blk = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
   const __half* x = tensor ? k : q;
 
   load_block_to_lds<D>(kp, x, b, h, blk, Y);
-  __syncthreads();
-  rope_lds<D, ROT == 2>(kp, tab, blk, Y);
+  rope_lds<D, ROT == 2>(kp, tab, blk, Y, coord);
   __syncthreads();
   __half* rcopy = tensor ? o.k_rope : o.q_rope;
   if (rcopy != nullptr) store_rope_copy<D>(kp, b, h, blk, Y, rcopy);
@@ -235,6 +248,7 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
   }
   amax = block_reduce_max(amax, red);
   const float s = fdiv_rn(amax, 7.0f);
+  const float rs = (s != 0.f) ? fdiv_rn(1.0f, s) : 0.f;
 
   float se = 0.f, sx = 0.f;
   uint8_t* codes = tensor ? o.k_codes : o.q_codes;
@@ -247,7 +261,15 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         float c = 0.f;
-        if (s != 0.f) c = fminf(fmaxf(rintf(fdiv_rn(v[r][j], s)), -7.f), 7.f);
+        if (s != 0.f) {
+          // rne(x / s) with IEEE division: x * float(1/s) is within 8.4e-7 of
+          // x / s (|x / s| <= 7), so away from the half-integers the rounding
+          // agrees; within 1e-6 of one the division is done exactly
+          float qd = fmul_rn(v[r][j], rs);
+          const float fr = qd - floorf(qd);
+          if (fabsf(fr - 0.5f) < 1e-6f) qd = fdiv_rn(v[r][j], s);
+          c = fminf(fmaxf(rintf(qd), -7.f), 7.f);
+        }
         const float e = fsub_rn(v[r][j], fmul_rn(s, c));
         se += e * e;
         sx += v[r][j] * v[r][j];
@@ -276,10 +298,10 @@ template <int D>
 __global__ __launch_bounds__(256) void rope_copy_kernel(KProblem kp, const __half* x, const float* tab,
                                                         __half* dst) {
   __shared__ float Y[kBlock][D + 4];
+  __shared__ int coord[kBlock][3];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   load_block_to_lds<D>(kp, x, b, h, blk, Y);
-  __syncthreads();
-  rope_lds<D>(kp, tab, blk, Y);
+  rope_lds<D>(kp, tab, blk, Y, coord);
   __syncthreads();
   store_rope_copy<D>(kp, b, h, blk, Y, dst);
 }
