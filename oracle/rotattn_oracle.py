@@ -74,7 +74,8 @@ def token_coords(L: int, prefix: int, grid) -> tuple[np.ndarray, np.ndarray]:
     idx = n - prefix
     video = idx >= 0
     ic = np.where(video, idx, 0)
-    coords = np.stack([ic // (Hh * W), (ic // W) % Hh, ic % W], axis=1)
+    hw, ww, hh = max(Hh * W, 1), max(W, 1), max(Hh, 1)      # a text-only sequence has an empty grid
+    coords = np.stack([ic // hw, (ic // ww) % hh, ic % ww], axis=1)
     return coords, video
 
 

@@ -131,3 +131,31 @@ def test_fp16_forward_strided():
             pp, bound = G.fp16_weight_bound(qr, kr, x["v"][b, h], L, D, np.arange(L))
             ref = pp["O"] / pp["l"][:, None]
             assert (np.abs(got[b, h] - ref) <= G.ATOL + G.RTOL * np.abs(ref) + bound).all()
+
+
+def test_prologue_rounding_ties():
+    """Q/K values that land exactly on half-integers of the quantization step: text-only tokens (no RoPE),
+    D = 64 (the rotation's 1/8 is exact), rows x = H y / 8 with y in {+-0.5, +-1.5, ..., +-6.5, +-7}, so the
+    rotated values are y and s = 1: every tie must round to even, as in the oracle."""
+    G.require_gpu()
+    w = W.WORKLOADS["smalld"].replace(H=1, grid=(0, 0, 0), prefix=128)
+    rng = np.random.default_rng(77)
+    halves = np.arange(-6.5, 7.0, 1.0)                      # -6.5 .. 6.5
+    H64 = np.array([[1.0]])
+    while H64.shape[0] < 64:
+        H64 = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), H64)
+    x = {}
+    for t in ("q", "k"):
+        y = rng.choice(halves, size=(128, 64))
+        y[:, 0] = 7.0                                        # absmax 7 in every token: s = 1 in every block
+        x[t] = ((y @ H64) / 8.0).astype(np.float16)[None, None]
+        assert np.array_equal(x[t][0, 0].astype(np.float64), (y @ H64) / 8.0)   # exact in fp16
+    x["v"] = rng.standard_normal((1, 1, 128, 64)).astype(np.float16)
+    p = G.R.problem_from_workload(w)
+    qk = G.R.rotattn_quantize_qk(p, G.dev(x["q"]), G.dev(x["k"]))
+    o = G.oracle_head(w, x, 0, 0)
+    for t in ("q", "k"):
+        assert np.array_equal(G.host(getattr(qk, f"{t}_scale"))[0, 0], np.ones(2, np.float32))
+        codes = G.unpack_qk_codes(G.host(getattr(qk, f"{t}_codes")))[0, 0]
+        assert np.array_equal(codes, o[t]["codes"]), t
+        assert (np.abs(o[t]["rot"][:, 1:] % 1.0 - 0.5) < 1e-12).all()   # every rotated value but dim 0 is a tie
