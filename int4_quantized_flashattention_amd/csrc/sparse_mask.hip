@@ -62,12 +62,16 @@ __global__ __launch_bounds__(256) void block_topn_kernel(KProblem kp, const floa
   const float* qs = q_bsum + bh * NB * D;
   const float* ks = k_bsum + bh * NB * D;
 
-  for (int e = tid; e < nrows * D; e += 256) {
+  for (int e = tid; e < kMaskRows * D; e += 256) {   // rows past the workgroup's: zeros (scored, not stored)
     const int r = e / D, d = e - r * D;
     const int i = i0 + r;
-    float v = qs[(long long)(2 * i) * D + d];
-    if (2 * i + 1 < NB) v = fadd_rn(v, qs[(long long)(2 * i + 1) * D + d]);
-    qh[r][d] = fdiv_rn(v, (float)min(kMaskQBlock, kp.L - kMaskQBlock * i));
+    float v = 0.f;
+    if (r < nrows) {
+      v = qs[(long long)(2 * i) * D + d];
+      if (2 * i + 1 < NB) v = fadd_rn(v, qs[(long long)(2 * i + 1) * D + d]);
+      v = fdiv_rn(v, (float)min(kMaskQBlock, kp.L - kMaskQBlock * i));
+    }
+    qh[r][d] = v;
   }
   __syncthreads();
   for (int j = tid; j < NB; j += 256) {
@@ -78,6 +82,7 @@ __global__ __launch_bounds__(256) void block_topn_kernel(KProblem kp, const floa
     for (int r = 0; r < kMaskRows; ++r) acc[r] = 0.f;
     auto chain = [&](auto full_tag) __attribute__((always_inline)) {
       constexpr bool kFull = decltype(full_tag)::value;
+#pragma unroll 8
       for (int d = 0; d < D; d += 4) {
         const float4 s4 = *reinterpret_cast<const float4*>(kj + d);
         const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
@@ -85,8 +90,7 @@ __global__ __launch_bounds__(256) void block_topn_kernel(KProblem kp, const floa
         for (int e = 0; e < 4; ++e) {
           const float kv = kFull ? sv[e] * 0.015625f : fdiv_rn(sv[e], (float)cnt);
 #pragma unroll
-          for (int r = 0; r < kMaskRows; ++r)
-            if (r < nrows) acc[r] = __builtin_fmaf(qh[r][d + e], kv, acc[r]);
+          for (int r = 0; r < kMaskRows; ++r) acc[r] = __builtin_fmaf(qh[r][d + e], kv, acc[r]);
         }
       }
     };
