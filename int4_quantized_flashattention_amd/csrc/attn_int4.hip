@@ -10,25 +10,27 @@
 // order; tiles routed to the FP16 path are skipped like masked blocks.
 //
 // Layout of the work (one workgroup = 4 waves = 128 query rows of one head):
-//  * S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 on E4M3 operands: the INT4
-//    codes are exact in E4M3 and the float32 sums of their products are exact
-//    integers, so this is the integer Q.K^T, delivered as floats (no
-//    int-to-float conversion per score). K codes are the A operand (rows =
-//    keys), Q codes the B operand (columns = queries). Each lane then owns
-//    one query column and 16 of the 32 keys of a 32 x 32 tile, so the row
-//    max and row sum are in-lane plus one exchange with lane ^ 32, and the P
-//    codes are already laid out as the B operand of the next product.
-//  * O^T = V^T P^T with the same FP8 instruction: V codes (A, rows = channels,
-//    stored by the V quantizer in exactly this operand order) as E4M3, times
-//    the P code bytes pq + 8 = rne(15 P) in [0, 15] as produced by
-//    v_cvt_pk_u8_f32 (B): read as E4M3 such a byte n is exactly n * 2^-9, so
-//    the float32 result is 2^-9 sum (pq + 8) v, exact; the zero-point
-//    correction rides inside it, as sum (pq + 8) v = sum pq v + 8 colsum(v)
-//    (integer identity). The float accumulator is rescaled in place when a
-//    row max grows.
+//  * S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 on FP6 E2M3 operands: the
+//    Q/K codes in [-7, 7] are exact in E2M3 and the float32 sums of their
+//    products are exact integers, so this is the integer Q.K^T, delivered as
+//    floats (no int-to-float conversion per score). K codes are the A operand
+//    (rows = keys), Q codes the B operand (columns = queries). Each lane then
+//    owns one query column and 16 of the 32 keys of a 32 x 32 tile, so the
+//    row max and row sum are in-lane plus one exchange with lane ^ 32, and the
+//    P codes are already laid out as the B operand of the next product.
+//  * O^T = V^T P^T with the same instruction on FP8 E4M3 operands: V codes (A,
+//    rows = channels, stored by the V quantizer in exactly this operand order)
+//    times the P code bytes pq + 8 = rne(15 P) in [0, 15], two per
+//    v_cvt_scalef32_pk_fp8_f32 (B): read as E4M3 such a byte n is exactly
+//    n * 2^-9, so the float32 result is 2^-9 sum (pq + 8) v, exact; the
+//    zero-point correction rides inside it, as sum (pq + 8) v = sum pq v +
+//    8 colsum(v) (integer identity). The float accumulator is rescaled in
+//    place when a row max grows.
 //  * A pre-pass expands each key block once into the exact LDS image of one
-//    pipeline stage (E4M3 K rows, int8 V rows); the loop copies images into
-//    LDS with direct-to-LDS loads, four stages deep where LDS allows.
+//    pipeline stage (FP6 K rows, E4M3 V^T rows); the loop copies images into
+//    LDS with direct-to-LDS loads, three or four stages deep.
+//  * Block-sparse instances (RainFusion2.0, section 3.1 mask M) visit only the
+//    key blocks the workgroup's mask row keeps.
 #include "common.h"
 
 #include <climits>
@@ -40,8 +42,7 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 
 // FP8 E4M3 byte of a 4-bit two's-complement code in [-8, 7]: every such
 // integer is exact in E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits),
-// so the FP8 matrix cores multiply the codes exactly, and their float32 sums over
-// at most 192 products of magnitude <= 49 are exact integers.
+// so the FP8 matrix cores multiply the V codes exactly.
 __device__ __forceinline__ uint32_t e4m3_of_code(uint32_t nib) {
   const uint32_t mag = (nib & 8u) ? 16u - nib : nib;   // 0..8
   const uint32_t byte = ((uint32_t)(0x4E4C4A4844403800ull >> (8 * (mag & 7u))) & 0xFFu) | (mag == 8u ? 0x50u : 0u);
@@ -138,7 +139,7 @@ constexpr int kFp6 = 2;
 template <int DP, int DV, int NW, int NST, int OCC, bool DUMP, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
-  constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP8 product each)
+  constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP6 product each)
   constexpr int NCT = DV / 32;             // 32-channel output tiles
   constexpr int QROW = DP / 2;             // packed code bytes per token
   constexpr int KST = kv_kst(DP);
