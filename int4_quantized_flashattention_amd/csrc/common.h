@@ -39,26 +39,11 @@ __device__ __forceinline__ float fadd_rn(float a, float b) { return __fadd_rn(a,
 __device__ __forceinline__ float fsub_rn(float a, float b) { return __fsub_rn(a, b); }
 __device__ __forceinline__ float fdiv_rn(float a, float b) { return __fdiv_rn(a, b); }
 
-// INT4 nibbles -> int8 lanes scaled by 16: low nibbles of w, then high nibbles of w.
-// (w << 4) & 0xF0F0F0F0 moves each low nibble to the top of its byte, keeping its
-// sign bit as the byte's sign; w & 0xF0F0F0F0 keeps the high nibbles in place.
-__device__ __forceinline__ int nib_lo16(uint32_t w) { return (int)((w << 4) & 0xF0F0F0F0u); }
-__device__ __forceinline__ int nib_hi16(uint32_t w) { return (int)(w & 0xF0F0F0F0u); }
-
-// 8 packed bytes (16 codes) -> a 16 x int8 matrix-core operand (each value times 16).
-__device__ __forceinline__ v4i unpack16(uint2 p) {
-  v4i r;
-  r[0] = nib_lo16(p.x);
-  r[1] = nib_hi16(p.x);
-  r[2] = nib_lo16(p.y);
-  r[3] = nib_hi16(p.y);
-  return r;
-}
-
 // LDS stage of one 64-key block in the INT4 attention kernel, and the byte image
 // of it in HBM that the kernel copies with direct-to-LDS loads: 64 K rows of DP
-// int8 operand bytes, then DV V channel rows of 64 int8 operand bytes. Within a
-// row the 16-byte pieces are permuted by kv_swz so that 8 or 16 consecutive
+// bytes (FP6 E2M3 operands: each run of 32 dims in a 32-byte slot, 24 bytes of
+// values and 8 unused), then DV V channel rows of 64 E4M3 operand bytes. Within
+// a row the 16-byte pieces are permuted by kv_swz so that 8 or 16 consecutive
 // rows read at the same logical piece fall in distinct LDS banks. Every size is
 // a multiple of 4096 bytes, so each thread of a 256-thread workgroup copies the
 // same number of 16-byte pieces.

@@ -1,10 +1,13 @@
-// Q/K prologue: 3D RoPE -> Walsh-Hadamard rotation -> per-64-token INT4
-// quantization with nibble-packed stores and the block error flag.
+// Q/K prologue: 3D RoPE -> RoPE-aware rotation -> per-64-token INT4
+// quantization with nibble-packed stores and the block error flag; optionally
+// the RoPE'd copies for the FP16 path and the block sums for block sparsity.
 //
 // Method: RotateAttention abstract (arXiv 2607.02584) -- 3D RoPE on Q and K,
-// a RoPE-aware orthonormal rotation applied after RoPE (here the online
-// Walsh-Hadamard variant), symmetric INT4 quantization, and selective FP16
-// fallback for blocks whose quantization error is too large.
+// a RoPE-aware orthonormal rotation (the online Walsh-Hadamard after RoPE, over
+// the head dim or per RoPE group, or the mergeable per-pair rotation folded
+// into RoPE's angles), symmetric INT4 quantization, and selective FP16
+// fallback for blocks whose quantization error is too large. Block sums:
+// RainFusion2.0, section 3.2 (block means as representative tokens).
 //
 // One workgroup of 256 threads handles one 64-token block of one (b, h,
 // tensor). The block is read once with 16-byte loads, rotated in registers
@@ -15,8 +18,8 @@
 // RoPE product and sum is rounded separately (no FMA; the library is built
 // with -ffp-contract=off and uses __fmul_rn and friends), the Hadamard
 // butterflies run in stage order h = 1, 2, 4, ..., then one multiply by
-// float(1/sqrt(n)); scale = absmax / 7 and code = rne(x / scale) with IEEE
-// division.
+// float(1/sqrt(n)); scale = absmax / 7 and code = rne(x / scale) as with
+// IEEE division (x * float(1/scale), divided exactly near rounding ties).
 #include "common.h"
 
 namespace rotattn {
