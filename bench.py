@@ -8,8 +8,8 @@ rotattn_quantize_v (per-channel INT4 V + column sums) -> rotattn_attention
 Metric: attention TOPS = 4 B H L^2 D / step time (D the nominal head dim),
 on the 720p-style workload (B=1, H=40, L=75600, D=128). The roofline entry
 reports the INT4 attention kernel alone against the INT8 matrix-core peak
-(5.0 POP/s dense; the INT4 codes are multiplied exactly on the FP8 matrix path,
-whose dense peak is the same). The CPU baseline is the oracle (numpy) on a bounded
+(5.0 POP/s dense; the INT4 codes are multiplied exactly on the FP6 matrix path,
+whose dense rate is twice that). The CPU baseline is the oracle (numpy) on a bounded
 sample of the same workload.
 
 With --sparse F the step is the block-sparse path instead (RainFusion2.0

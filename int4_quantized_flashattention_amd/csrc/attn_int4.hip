@@ -18,16 +18,16 @@
 //    owns one query column and 16 of the 32 keys of a 32 x 32 tile, so the
 //    row max and row sum are in-lane plus one exchange with lane ^ 32, and the
 //    P codes are already laid out as the B operand of the next product.
-//  * O^T = V^T P^T with the same instruction on FP8 E4M3 operands: V codes (A,
-//    rows = channels, stored by the V quantizer in exactly this operand order)
-//    times the P code bytes pq + 8 = rne(15 P) in [0, 15], two per
-//    v_cvt_scalef32_pk_fp8_f32 (B): read as E4M3 such a byte n is exactly
-//    n * 2^-9, so the float32 result is 2^-9 sum (pq + 8) v, exact; the
-//    zero-point correction rides inside it, as sum (pq + 8) v = sum pq v +
-//    8 colsum(v) (integer identity). The float accumulator is rescaled in
-//    place when a row max grows.
+//  * O^T = V^T P^T with the same instruction, again on FP6 E2M3 operands: V
+//    codes (A, rows = channels; in [-7, 7], exact in E2M3) times the P codes
+//    pq + 8 = rne(15 P) in [0, 15] (B), all 32 of a lane from one
+//    v_cvt_scalef32_2xpk16_fp6_f32: as E2M3 such a code n is exactly n * 2^-3,
+//    so the float32 result is 2^-3 sum (pq + 8) v, exact; the zero-point
+//    correction rides inside it, as sum (pq + 8) v = sum pq v + 8 colsum(v)
+//    (integer identity). FP6 on both sides takes half the matrix-core cycles
+//    of FP8. The float accumulator is rescaled in place when a row max grows.
 //  * A pre-pass expands each key block once into the exact LDS image of one
-//    pipeline stage (FP6 K rows, E4M3 V^T rows); the loop copies images into
+//    pipeline stage (FP6 K rows, FP6 V^T rows); the loop copies images into
 //    LDS with direct-to-LDS loads, three or four stages deep.
 //  * Block-sparse instances (RainFusion2.0, section 3.1 mask M) visit only the
 //    key blocks the workgroup's mask row keeps.
@@ -40,14 +40,6 @@ namespace rotattn {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// FP8 E4M3 byte of a 4-bit two's-complement code in [-8, 7]: every such
-// integer is exact in E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits),
-// so the FP8 matrix cores multiply the V codes exactly.
-__device__ __forceinline__ uint32_t e4m3_of_code(uint32_t nib) {
-  const uint32_t mag = (nib & 8u) ? 16u - nib : nib;   // 0..8
-  const uint32_t byte = ((uint32_t)(0x4E4C4A4844403800ull >> (8 * (mag & 7u))) & 0xFFu) | (mag == 8u ? 0x50u : 0u);
-  return byte | ((nib & 8u) ? 0x80u : 0u);
-}
 // FP6 E2M3 bits (sign, 2 exponent bits with bias 1, 3 mantissa bits) of a
 // 4-bit two's-complement code in [-7, 7]: every such integer is exact in E2M3
 // (7 = 1.75 * 2^2), so the FP6 matrix path also multiplies the codes exactly.
@@ -70,32 +62,31 @@ __device__ __forceinline__ void e2m3_pack32(uint4 p, uint32_t (&o)[6]) {
   }
 }
 
-// 16 packed bytes in the operand order of the V codes (for each 4-byte word: the
-// four low nibbles, then the four high nibbles) -> 32 E4M3 bytes in that order
-__device__ __forceinline__ void e4m3_expand32_split(uint4 p, uint4& lo, uint4& hi) {
+// The 16 V code bytes of one channel and lane half hh (byte 8 s + 4 w + b holds
+// key 32 s + 16 w + 4 hh + b in its low nibble, that key + 8 in its high one)
+// -> the 24-byte FP6 operand whose element 2 v + s is the key of S^T value v
+// of half s (32 s + 8 (v / 4) + 4 hh + v % 4): the element order in which
+// v_cvt_scalef32_2xpk16_fp6_f32 interleaves its two 16-float sources.
+__device__ __forceinline__ void e2m3_pack32_v(uint4 p, uint32_t (&o)[6]) {
   const uint32_t w[4] = {p.x, p.y, p.z, p.w};
-  uint32_t o[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t l = 0, h = 0;
+  for (int k = 0; k < 6; ++k) o[k] = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t byte = (w[i] >> (8 * b)) & 0xFFu;
-      l |= e4m3_of_code(byte & 15u) << (8 * b);
-      h |= e4m3_of_code(byte >> 4) << (8 * b);
-    }
-    o[2 * i] = l;
-    o[2 * i + 1] = h;
+  for (int i = 0; i < 32; ++i) {
+    const int s = i & 1, v = i >> 1;
+    const uint32_t byte = (w[2 * s + (v >> 3)] >> (8 * (v & 3))) & 0xFFu;
+    const uint32_t e = e2m3_of_code(((v >> 2) & 1) ? byte >> 4 : byte & 15u);
+    const int bit = 6 * i, k = bit >> 5, sh = bit & 31;
+    o[k] |= e << sh;
+    if (sh > 26) o[k + 1] |= e >> (32 - sh);
   }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // Expands one (b, h, key block) into the LDS image the attention kernel copies:
 // the packed K codes of its 64 keys become FP6 E2M3 operands (each run of 32
-// dims in a 32-byte slot: 24 bytes of packed values, 8 unused), and the
-// operand-order V codes of its channels E4M3 bytes in the same operand order,
-// all at their permuted LDS offsets.
+// dims in a 32-byte slot: 24 bytes of packed values, 8 unused), and the V
+// codes of each channel FP6 operands in the same slots (32 keys per slot, in
+// the element order of the P operand), all at their permuted LDS offsets.
 template <int DP, int DV>
 __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_t* __restrict__ k_codes,
                                                        const uint8_t* __restrict__ v_codes, uint8_t* image) {
@@ -115,11 +106,11 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
     *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
   }
   for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16) {
-    const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);
-    uint4 lo, hi;
-    e4m3_expand32_split(*reinterpret_cast<const uint4*>(vg + o), lo, hi);
-    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = lo;
-    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = hi;
+    const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);   // c = 2 hh
+    uint32_t f6[6];
+    e2m3_pack32_v(*reinterpret_cast<const uint4*>(vg + o), f6);
+    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
   }
 }
 
@@ -127,11 +118,11 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
 constexpr int kFp6 = 2;
 
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
-// 64, the block's LDS image (FP6 K rows, E4M3 V^T rows, the K scale) arrives in
+// 64, the block's LDS image (FP6 K rows, FP6 V^T rows, the K scale) arrives in
 // one stage of an NST-stage ring through direct-to-LDS loads issued NST - 1
 // blocks ahead; one barrier per block. Every wave computes S^T of its 32
 // queries (FP6 products), the online softmax and P codes in registers, and
-// O^T on the FP8 matrix cores into a float32 accumulator kept at the running
+// O^T on the FP6 matrix path into a float32 accumulator kept at the running
 // max, rescaled only when some row max of the wave grows.
 // SPARSE: block-sparse attention (RainFusion2.0, section 3.1: Q_i K_j^T and
 // P_ij V_j are skipped where M_ij = 0), with one mask row per 128-row query
@@ -285,14 +276,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     lds_copy4(kscale + j, lds_addr(kscale_slot(s_tag)));
   };
 
-  // O^T accumulates on the FP8 matrix cores in float32. The V codes are E4M3
-  // (exact integers), and the P code byte n = pq + 8 that v_cvt_pk_u8_f32
-  // produces, read as E4M3, is exactly n * 2^-9 (a subnormal below 8), so each
-  // block adds 2^-9 * sum (pq + 8) v exactly. o is kept at the running max:
-  // when a row max of the wave grows it is rescaled in place.
+  // O^T accumulates on the FP6 matrix path in float32. The V codes are E2M3
+  // (exact integers), and the P code n = pq + 8 is the E2M3 value n * 2^-3
+  // (a subnormal below 8), so each block adds 2^-3 * sum (pq + 8) v exactly.
+  // o is kept at the running max: when a row max of the wave grows it is
+  // rescaled in place.
   float m_run = -INFINITY;
   float l15 = 0.f;                 // row sum of 15 P (lane-partial), at m_run
-  v16f o[NCT];                     // 2^-9 * sum (pq + 8) v, at m_run
+  v16f o[NCT];                     // 2^-3 * sum (pq + 8) v, at m_run
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -307,6 +298,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   for (int c = 0; c < 2 * NC; ++c) koff[c] = col * DP + 16 * ((4 * (c >> 1) + 2 * hh + (c & 1)) ^ kv_swz(DP, col));
 #pragma unroll
   for (int s = 0; s < 2; ++s) voff[s] = col * 64 + 16 * ((2 * hh + s) ^ kv_swz(64, col));
+  // Each operand is a 16-byte and an 8-byte LDS read that must land in six
+  // consecutive registers. Two 8-byte reads from one base register get paired
+  // into a single read2 instruction, which then needs register moves; an
+  // opaque base register of its own for every 8-byte read (of K row col + 32
+  // and of each V tile) keeps them apart.
+  int khi[NC], vhi[NCT];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    khi[c] = koff[2 * c + 1] + 32 * DP;
+    asm volatile("" : "+v"(khi[c]));
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    vhi[ct] = voff[1] + ct * 32 * 64;
+    if (ct > 0) asm volatile("" : "+v"(vhi[ct]));
+  }
 
   // S^T of the block in `stage` (the integer q.k as exact floats), as two
   // 32-key halves, on the FP6 matrix path (E2M3 codes, no block scaling)
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       const v4i a0l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c]);
       const v2i a0h = *reinterpret_cast<const v2i*>(Ks + koff[2 * c + 1]);
       const v4i a1l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c] + 32 * DP);
-      const v2i a1h = *reinterpret_cast<const v2i*>(Ks + koff[2 * c + 1] + 32 * DP);
+      const v2i a1h = *reinterpret_cast<const v2i*>(Ks + khi[c]);
       const v8i a0 = v8i{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], 0, 0};
       const v8i a1 = v8i{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], 0, 0};
       d0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], d0, kFp6, kFp6, 0, 0, 0, 0);
@@ -372,14 +379,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       l15 *= alpha;
       m_run = m_new;
     }
-    // 15 P = 2^(acc c - (m - log2 15)); its rne is the code byte pq + 8. Two
-    // codes per instruction: v_cvt_scalef32_pk_fp8_f32 converts 15P / 2^9 to
-    // E4M3, whose grid below 2^-5 is exactly the multiples of 2^-9, so with
-    // round-to-nearest-even the byte is rne(15P) (the E4M3 bit pattern of
-    // n * 2^-9 is n for n < 16) -- the same byte v_cvt_pk_u8_f32 gives.
+    // 15 P = 2^(acc c - (m - log2 15)); its rne is the code pq + 8. All 32
+    // codes of the lane come from one v_cvt_scalef32_2xpk16_fp6_f32, which
+    // converts 15P / 2^3 to E2M3 with round-to-nearest-even: the E2M3 grid
+    // below 2 is exactly the multiples of 2^-3, so each element is
+    // rne(15P) * 2^-3, whose six bits read as an integer are rne(15P).
+    // Element 2 v + s of the result is value v of half s.
     const float nm15 = -fsub_rn(m_run, log2_15);
-    v4i pop[2];
-    float ls0 = 0.f, ls1 = 0.f;
+    if (DUMP && wrow + col < L) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
+          a.d_acc[((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key] = (int)(s == 0 ? s0[v] : s1[v]);
+        }
+    }
     if constexpr (!kRagged && !DUMP) {
       // full block: every exponent first (in place, S^T is not needed after
       // this), then every exp2, so that the two run as independent streams
@@ -389,49 +404,38 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
       for (int v = 0; v < 16; ++v) { s0[v] = exp2_hw(s0[v]); s1[v] = exp2_hw(s1[v]); }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    } else {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        float p15[4];
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int v = 4 * kq + bb;
-          if constexpr (!kRagged && !DUMP) {
-            p15[bb] = s == 0 ? s0[v] : s1[v];
-          } else {
-            float t = fmaf(s == 0 ? s0[v] : s1[v], cs, nm15);
-            if (kRagged) {
-              const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
-              if (key >= L) t = -INFINITY;
-            }
-            p15[bb] = exp2_hw(t);
-          }
-          if (bb & 1) ls1 += p15[bb]; else ls0 += p15[bb];
+      for (int v = 0; v < 16; ++v) {
+        float t0 = fmaf(s0[v], cs, nm15), t1 = fmaf(s1[v], cs, nm15);
+        if (kRagged) {
+          const int key = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key >= L) t0 = -INFINITY;
+          if (key + 32 >= L) t1 = -INFINITY;
         }
-        // both halves of w are written below, so its initial value does not
-        // matter: an empty asm defines the register without an instruction
-        v2s16 w;
-        asm volatile("" : "=v"(w));
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p15[0], p15[1], 512.0f, false);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, p15[2], p15[3], 512.0f, true);
-        const uint32_t word = (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
-        if (DUMP && wrow + col < L) {
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int v = 4 * kq + bb;
-            const int key = key0 + 32 * s + 8 * kq + 4 * hh + bb;
-            const long long di = ((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key;
-            a.d_acc[di] = (int)(s == 0 ? s0[v] : s1[v]);
-            a.d_pq[di] = (int8_t)((int)((word >> (8 * bb)) & 0xFFu) - 8);
-          }
-        }
-        pop[s][kq] = (int)word;
+        s0[v] = exp2_hw(t0);
+        s1[v] = exp2_hw(t1);
       }
+    }
+    float ls0 = s0[0], ls1 = s1[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) { ls0 += s0[v]; ls1 += s1[v]; }
     l15 += ls0 + ls1;
+    const auto p6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 8.0f);
+    if (DUMP && wrow + col < L) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
+          const int bit = 6 * (2 * v + s), k = bit >> 5, sh = bit & 31;
+          uint32_t e = (uint32_t)p6[k] >> sh;
+          if (sh > 26) e |= (uint32_t)p6[k + 1] << (32 - sh);
+          a.d_pq[((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key] = (int8_t)((int)(e & 63u) - 8);
+        }
+    }
     // O^T += V^T (pq + 8)^T: the zero-point correction rides inside the product
-    const v8i pb = v8i{pop[0][0], pop[0][1], pop[0][2], pop[0][3], pop[1][0], pop[1][1], pop[1][2], pop[1][3]};
+    const v8i pb = v8i{(int)p6[0], (int)p6[1], (int)p6[2], (int)p6[3], (int)p6[4], (int)p6[5], 0, 0};
     // raised wave priority while this wave issues its matrix products (P.V
     // here, S^T of the next block after it), so the matrix cores are fed
     // promptly while the other waves of the SIMD run their softmax
@@ -439,25 +443,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     const long long r = (long long)unit_idx * kBlock + 32 * wave + col;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
+      // the 24 bytes of channel row ct * 32 + col's slot for this lane half
       const v4i vl = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[0]);
-      const v4i vh = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[1]);
-      const v8i va = v8i{vl[0], vl[1], vl[2], vl[3], vh[0], vh[1], vh[2], vh[3]};
+      const v2i vh = *reinterpret_cast<const v2i*>(Vs + vhi[ct]);
+      const v8i va = v8i{vl[0], vl[1], vl[2], vl[3], vh[0], vh[1], 0, 0};
       if constexpr (DUMP) {
         // this block's sum alone, to expose the integers sum (pq + 8) v
         v16f z;
 #pragma unroll
         for (int v = 0; v < 16; ++v) z[v] = 0.f;
-        const v16f blk = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, z, 0, 0, 0, 0, 0, 0);
+        const v16f blk = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, z, kFp6, kFp6, 0, 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           o[ct][v] += blk[v];
           if (wrow + col < L) {
             const int ch = ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            a.d_pv[(r * NB + j) * DV + ch] = (int)(blk[v] * 512.0f);
+            a.d_pv[(r * NB + j) * DV + ch] = (int)(blk[v] * 8.0f);
           }
         }
       } else {
-        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[ct], 0, 0, 0, 0, 0, 0);
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[ct], kFp6, kFp6, 0, 0, 0, 0);
       }
     }
     if (DUMP && wrow + col < L && hh == 0) a.d_m[r * NB + j] = m_run;
@@ -537,9 +542,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   if (row >= L) return;
   const float* svp = a.v_scale + (long long)bh * DV;
   if (!mixed) {
-    // out = O (s_v / 15) / l with O = 2^9 o and l = l15 / 15 (a sparse row
+    // out = O (s_v / 15) / l with O = 2^3 o and l = l15 / 15 (a sparse row
     // that keeps no key block gets zeros)
-    const float inv = (SPARSE && l15t == 0.f) ? 0.f : 512.0f / l15t;
+    const float inv = (SPARSE && l15t == 0.f) ? 0.f : 8.0f / l15t;
     __half* orow = a.out + (long long)b * kp.sb + (long long)h * kp.sh + (long long)row * kp.sl;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -559,11 +564,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
       for (int g = 0; g < 4; ++g) {
         const int ch = ct * 32 + 8 * g + 4 * hh;
         float4 f;
-        // O (s_v / 15) with O = 2^9 o
-        f.x = o[ct][4 * g + 0] * (svp[ch + 0] * (512.0f / 15.0f));
-        f.y = o[ct][4 * g + 1] * (svp[ch + 1] * (512.0f / 15.0f));
-        f.z = o[ct][4 * g + 2] * (svp[ch + 2] * (512.0f / 15.0f));
-        f.w = o[ct][4 * g + 3] * (svp[ch + 3] * (512.0f / 15.0f));
+        // O (s_v / 15) with O = 2^3 o
+        f.x = o[ct][4 * g + 0] * (svp[ch + 0] * (8.0f / 15.0f));
+        f.y = o[ct][4 * g + 1] * (svp[ch + 1] * (8.0f / 15.0f));
+        f.z = o[ct][4 * g + 2] * (svp[ch + 2] * (8.0f / 15.0f));
+        f.w = o[ct][4 * g + 3] * (svp[ch + 3] * (8.0f / 15.0f));
         *reinterpret_cast<float4*>(po + ch) = f;
       }
     if (hh == 0) {

@@ -41,7 +41,7 @@ __device__ __forceinline__ float fdiv_rn(float a, float b) { return __fdiv_rn(a,
 // LDS stage of one 64-key block in the INT4 attention kernel, and the byte image
 // of it in HBM that the kernel copies with direct-to-LDS loads: 64 K rows of DP
 // bytes (FP6 E2M3 operands: each run of 32 dims in a 32-byte slot, 24 bytes of
-// values and 8 unused), then DV V channel rows of 64 E4M3 operand bytes. Within
+// values and 8 unused), then DV V channel rows of two such FP6 slots. Within
 // a row the 16-byte pieces are permuted by kv_swz so that 8 or 16 consecutive
 // rows read at the same logical piece fall in distinct LDS banks. Every size is
 // a multiple of 4096 bytes, so each thread of a 256-thread workgroup copies the
