@@ -109,18 +109,30 @@ __device__ __forceinline__ void rope_lds(const KProblem& kp, const float* tab, i
   const float* ctab = tab + kp.tab_off[a] + pr;
   const float* stab = ctab + npos * kp.npair[a];
   const int stride = kp.npair[a];
-  for (int tok = tid >> 6; tok < kBlock; tok += 4) {
+  // this thread's 16 tokens: every table load first (one memory latency, not
+  // sixteen), then the rotations; tokens past L and text tokens read
+  // position 0 and are left alone (text tokens turn by the pair angle alone
+  // with PAIR)
+  constexpr int NT = kBlock / 4;
+  float cv[NT], sv[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int tok = (tid >> 6) + 4 * i;
+    const int tg = blk * kBlock + tok;
+    const int pos = (tg < kp.L && tg >= kp.prefix) ? coord[tok][a] : 0;
+    cv[i] = ctab[pos * stride];
+    sv[i] = stab[pos * stride];
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int tok = (tid >> 6) + 4 * i;
     const int tg = blk * kBlock + tok;
     if (tg >= kp.L) break;
-    float c, s;
+    float c = cv[i], s = sv[i];
     if (tg < kp.prefix) {
       if (!PAIR) continue;
       c = kp.pair_c;
       s = kp.pair_s;
-    } else {
-      const int pos = coord[tok][a];
-      c = ctab[pos * stride];
-      s = stab[pos * stride];
     }
     const float x0 = Y[tok][d0], x1 = Y[tok][d0 + 1];
     Y[tok][d0] = fsub_rn(fmul_rn(x0, c), fmul_rn(x1, s));
@@ -145,6 +157,16 @@ __device__ __forceinline__ void store_rope_copy(const KProblem& kp, int b, int h
     for (int e = 0; e < 8; ++e) hv[e] = __float2half_rn(Y[tok][part * PER + c * 8 + e]);
     reinterpret_cast<uint4*>(d)[c] = u;
   }
+}
+
+// v of lane ^ MASK (MASK 1 or 2) within the lane's aligned group of four, by
+// a DPP quad permutation (no LDS round trip). The 32-value chunks of one
+// token sit in consecutive lanes from a multiple of PARTS (4, or 2 and 6 with
+// MASK 1 only), so the Hadamard partners of stages 32 and 64 are such lanes.
+template <int MASK>
+__device__ __forceinline__ float quad_xor(float v) {
+  constexpr int kQuadPerm = MASK == 1 ? 0xB1 : 0x4E;   // [1,0,3,2] : [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kQuadPerm, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float block_reduce_max(float v, float* red) {
@@ -237,7 +259,7 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
         const bool upper = (part & mask) != 0;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-          const float other = __shfl_xor(v[r][j], mask);
+          const float other = mask == 1 ? quad_xor<1>(v[r][j]) : quad_xor<2>(v[r][j]);
           v[r][j] = upper ? fsub_rn(other, v[r][j]) : fadd_rn(v[r][j], other);
         }
       }
@@ -261,18 +283,30 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
     if (task < TASKS) {
       const int tok = task / PARTS, part = task - (task / PARTS) * PARTS;
       uint32_t words[4] = {0u, 0u, 0u, 0u};
+      // rne(x / s) with IEEE division: x * float(1/s) is within 8.4e-7 of
+      // x / s (|x / s| <= 7), so away from the half-integers the rounding
+      // agrees; within 1e-6 of one the division is done exactly. The
+      // divisions sit behind a wave-uniform branch taken only when some lane
+      // of the wave has such a value (otherwise the compiler evaluates them
+      // for every element and selects).
+      float qd[32];
+      bool near_tie = false;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        float c = 0.f;
-        if (s != 0.f) {
-          // rne(x / s) with IEEE division: x * float(1/s) is within 8.4e-7 of
-          // x / s (|x / s| <= 7), so away from the half-integers the rounding
-          // agrees; within 1e-6 of one the division is done exactly
-          float qd = fmul_rn(v[r][j], rs);
-          const float fr = qd - floorf(qd);
-          if (fabsf(fr - 0.5f) < 1e-6f) qd = fdiv_rn(v[r][j], s);
-          c = fminf(fmaxf(rintf(qd), -7.f), 7.f);
+        qd[j] = fmul_rn(v[r][j], rs);
+        const float fr = qd[j] - floorf(qd[j]);
+        near_tie |= fabsf(fr - 0.5f) < 1e-6f;
+      }
+      if (__builtin_amdgcn_ballot_w64(near_tie && s != 0.f) != 0ull) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float fr = qd[j] - floorf(qd[j]);
+          if (s != 0.f && fabsf(fr - 0.5f) < 1e-6f) qd[j] = fdiv_rn(v[r][j], s);
         }
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float c = (s != 0.f) ? fminf(fmaxf(rintf(qd[j]), -7.f), 7.f) : 0.f;
         const float e = fsub_rn(v[r][j], fmul_rn(s, c));
         se += e * e;
         sx += v[r][j] * v[r][j];
