@@ -277,12 +277,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   // compiler keeps the copy's stage static), so that every wave issues NVM
   // vector-memory instructions per block.
   const float* kscale = a.k_scale + (long long)bh * NB;
+  // Per-thread byte offsets of the pieces stay in registers for the whole
+  // loop; the block's image base goes in scalar registers.
+  uint32_t voffs[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) voffs[i] = (uint32_t)(toff + i * NT * 16);
   auto dma_block = [&](int j, auto s_tag) __attribute__((always_inline)) {
-    const uint8_t* src = img + (long long)j * IMG;
+    const uint64_t src = uniform_ptr(img + (long long)j * IMG);
     const uint32_t dst = lds_addr(stage(s_tag)) + wave_u * 1024;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) lds_copy16(src + (toff + i * NT * 16), dst + i * NT * 16);
-    lds_copy4(kscale + j, lds_addr(kscale_slot(s_tag)));
+    for (int i = 0; i < NDMA; ++i) lds_copy16_s(src, voffs[i], dst + i * NT * 16);
+    lds_copy4_s(uniform_ptr(kscale + j), 0u, lds_addr(kscale_slot(s_tag)));
   };
 
   // O^T accumulates on the FP6 matrix path in float32. The V codes are E2M3

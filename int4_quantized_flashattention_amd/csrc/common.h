@@ -89,6 +89,30 @@ __device__ __forceinline__ void lds_copy4(const void* src, uint32_t m0) {
       : "memory");
 }
 
+// A wave-uniform pointer in scalar registers: each 32-bit half goes through
+// readfirstlane (whose result is a signed int: cast to uint32_t before
+// widening, or the low half would be sign-extended into the high one).
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+  const uint64_t a = (uint64_t)p;
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+}
+// The same copies addressed as a wave-uniform base in scalar registers plus a
+// 32-bit per-lane byte offset: no 64-bit vector address per copy, and M0 is
+// set without saving it (declared clobbered).
+__device__ __forceinline__ void lds_copy16_s(uint64_t base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4_s(uint64_t base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
 // Workgroup barrier without a memory fence: LDS stages are filled by
 // direct-to-LDS loads whose completion the caller has already waited for.
 __device__ __forceinline__ void stage_barrier() {
