@@ -282,12 +282,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   uint32_t voffs[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) voffs[i] = (uint32_t)(toff + i * NT * 16);
+  const uint64_t img_s = uniform_ptr(img), ksc_s = uniform_ptr(kscale);
   auto dma_block = [&](int j, auto s_tag) __attribute__((always_inline)) {
-    const uint64_t src = uniform_ptr(img + (long long)j * IMG);
+    const uint64_t src = img_s + (uint64_t)j * IMG;
     const uint32_t dst = lds_addr(stage(s_tag)) + wave_u * 1024;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) lds_copy16_s(src, voffs[i], dst + i * NT * 16);
-    lds_copy4_s(uniform_ptr(kscale + j), 0u, lds_addr(kscale_slot(s_tag)));
+    lds_copy4_s(ksc_s + 4ull * (uint64_t)j, 0u, lds_addr(kscale_slot(s_tag)));
   };
 
   // O^T accumulates on the FP6 matrix path in float32. The V codes are E2M3
