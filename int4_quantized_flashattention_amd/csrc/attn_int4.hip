@@ -240,30 +240,33 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     cq = fmul_rn(a.q_scale[bh * NB + qblk], c0);
   }
 
-  const uint8_t* kflag = a.route ? a.k_flag + (long long)bh * NB : nullptr;
+  // wave-uniform bases of the key-block flags and of the mask row (0: none)
+  const uint64_t kflag_s = a.route ? uniform_ptr(a.k_flag + (long long)bh * NB) : 0ull;
   // Block-sparse: the bit row (words of 32 key blocks) of the 128-row query
   // block this workgroup covers; every wave processes exactly the key blocks
   // the loop visits.
   const int MW = a.mask_words;
-  const uint32_t* mrow = nullptr;
-  if constexpr (SPARSE) mrow = a.block_mask + ((long long)bh * ((NB + 1) / 2) + row_base / kMaskQBlock) * MW;
+  uint64_t mrow_s = 0;
+  if constexpr (SPARSE)
+    mrow_s = uniform_ptr(a.block_mask + ((long long)bh * ((NB + 1) / 2) + row_base / kMaskQBlock) * MW);
   // the next key block at or after j that this path takes (NB if none); the
-  // result is wave-uniform, which keeps the loop control in scalar registers
+  // result is wave-uniform and formed from scalar loads, which keeps the loop
+  // control in scalar registers
   auto next_block = [&](int j) __attribute__((always_inline)) {
     if constexpr (SPARSE) {
       if (j >= NB) return NB;
       int w = j >> 5;
-      uint32_t bits = uniform_word(mrow, w) & (~0u << (j & 31));
+      uint32_t bits = uniform_word_u(mrow_s, w) & (~0u << (j & 31));
       while (bits == 0) {
         if (++w >= MW) return NB;
-        bits = uniform_word(mrow, w);
+        bits = uniform_word_u(mrow_s, w);
       }
-      j = __builtin_amdgcn_readfirstlane(32 * w + __builtin_ctz(bits));
+      j = 32 * w + __builtin_ctz(bits);
       return j < NB ? j : NB;
     } else {
-      if (kflag != nullptr)
-        while (j < NB && uniform_byte(kflag, j) != 0) ++j;   // FP16 tile: the other path takes it
-      return __builtin_amdgcn_readfirstlane(j);
+      if (kflag_s != 0ull)
+        while (j < NB && uniform_byte_u(kflag_s, j) != 0) ++j;   // FP16 tile: the other path takes it
+      return j;
     }
   };
   // Block j's image goes to LDS stage `stage` with NDMA direct-to-LDS loads per

@@ -147,6 +147,20 @@ __device__ __forceinline__ uint32_t uniform_word(const uint32_t* base, int i) {
   return *reinterpret_cast<const_u32p>(((uint64_t)hi << 32) | lo);
 }
 
+// The same reads from a base already made uniform by uniform_ptr, with a
+// wave-uniform index: the address is formed in scalar registers, with no
+// readfirstlane per access.
+__device__ __forceinline__ uint32_t uniform_byte_u(uint64_t base, int i) {
+  const uint64_t addr = base + (uint64_t)(int64_t)i;
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
+  const uint32_t w = *reinterpret_cast<const_u32p>(addr & ~3ull);
+  return (w >> (8 * ((uint32_t)addr & 3u))) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t uniform_word_u(uint64_t base, int i) {
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
+  return *reinterpret_cast<const_u32p>(base + 4ull * (uint64_t)(int64_t)i);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
