@@ -113,38 +113,46 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
 #pragma unroll
   for (int su = 0; su < 4; ++su) voff[su] = VT0 + col * 128 + 16 * ((2 * su + hh) ^ kv_swz(128, col));
 
-  const uint8_t* kflag = a.route ? a.k_flag + (long long)bh * NB : nullptr;
+  // wave-uniform base of the key-block flags (0: no routing)
+  const uint64_t kflag_s = a.route ? uniform_ptr(a.k_flag + (long long)bh * NB) : 0ull;
   // key blocks this workgroup visits: all when some row runs whole on this
-  // path, else the flagged ones only (wave-uniform)
+  // path, else the flagged ones only (wave-uniform, from scalar loads)
   auto next_block = [&](int j) __attribute__((always_inline)) {
-    if (!any_full && kflag != nullptr)
-      while (j < NB && uniform_byte(kflag, j) == 0) ++j;
-    return __builtin_amdgcn_readfirstlane(j);
+    if (!any_full && kflag_s != 0ull)
+      while (j < NB && uniform_byte_u(kflag_s, j) == 0) ++j;
+    return j;
   };
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // thread tid fills LDS bytes [i * 4096 + 16 * tid, +16) of each stage; for the
   // K half that is row kr[i], physical piece kp_[i], holding logical piece
   // kp_[i] ^ swz(row) of key j * 64 + kr[i] (the last key row stands in past L:
   // those keys are masked out of S)
-  const __half* kbase = a.k_rope + (long long)bh * L * D;
-  const uint8_t* vimg = a.f16_vt + (long long)bh * NB * VTB + tid * 16;
-  int krow[NDK], kpiece[NDK];
+  // Copies address a wave-uniform base in scalar registers (the key block's
+  // first K row, the block's V^T image) plus a 32-bit lane offset within it.
+  const uint64_t kbase_s = uniform_ptr(a.k_rope + (long long)bh * L * D);
+  const uint64_t vimg_s = uniform_ptr(a.f16_vt + (long long)bh * NB * VTB);
+  int krow[NDK];
+  uint32_t kcol[NDK], voffs[NDV];
 #pragma unroll
   for (int i = 0; i < NDK; ++i) {
     const int o = i * 4096 + tid * 16;
     krow[i] = o / KROWB;
-    kpiece[i] = ((o % KROWB) >> 4) ^ f16_kswz<D>(krow[i]);
+    kcol[i] = (uint32_t)(16 * (((o % KROWB) >> 4) ^ f16_kswz<D>(krow[i])));   // byte offset in the row
   }
+#pragma unroll
+  for (int i = 0; i < NDV; ++i) voffs[i] = (uint32_t)(tid * 16 + i * 4096);
   auto dma_block = [&](int j, uint8_t* stage_base) __attribute__((always_inline)) {
     const uint32_t dst = lds_addr(stage_base) + wave_u * 1024;
+    const uint64_t ksrc = kbase_s + (uint64_t)j * (kBlock * 2 * D);
+    const int last = L - 1 - j * kBlock;   // rows past L repeat the last key (masked out of S)
 #pragma unroll
     for (int i = 0; i < NDK; ++i) {
-      const int key = min(j * kBlock + krow[i], L - 1);
-      lds_copy16(kbase + (long long)key * D + 8 * kpiece[i], dst + i * 4096);
+      const int r = min(krow[i], last);
+      lds_copy16_s(ksrc, (uint32_t)r * (uint32_t)(2 * D) + kcol[i], dst + i * 4096);
     }
-    const uint8_t* vsrc = vimg + (long long)j * VTB;
+    const uint64_t vsrc = vimg_s + (uint64_t)j * VTB;
 #pragma unroll
-    for (int i = 0; i < NDV; ++i) lds_copy16(vsrc + i * 4096, dst + VT0 + i * 4096);
+    for (int i = 0; i < NDV; ++i) lds_copy16_s(vsrc, voffs[i], dst + VT0 + i * 4096);
   };
 
   float m_run = -INFINITY, l_part = 0.f;
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
     uint8_t* oth = S == 0 ? stg1 : stg0;
     const int jn = (j + 1 < NB) ? next_block(j + 1) : NB;
     if (jn < NB) dma_block(jn, oth);
-    if (full || (mixed && uniform_byte(kflag, j) != 0)) {
+    if (full || (mixed && uniform_byte_u(kflag_s, j) != 0)) {
       compute(cur, j);
       __builtin_amdgcn_s_setprio(0);
     }
