@@ -189,16 +189,21 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
           mx = fmaxf(mx, sacc[s][v]);
         }
     } else {
-      float ma = fmaxf(sacc[0][0], sacc[1][0]), mb = fmaxf(sacc[0][1], sacc[1][1]);
+      // two interleaved max3 chains over the 32 values of this lane
+      float ma = smax3(sacc[0][0], sacc[1][0], sacc[0][2]);
+      float mb = smax3(sacc[0][1], sacc[1][1], sacc[0][3]);
 #pragma unroll
-      for (int v = 2; v < 16; v += 2) {
-        ma = fmaxf(fmaxf(ma, sacc[0][v]), sacc[1][v]);
-        mb = fmaxf(fmaxf(mb, sacc[0][v + 1]), sacc[1][v + 1]);
+      for (int v = 2; v < 14; v += 2) {
+        ma = smax3(ma, sacc[1][v], sacc[0][v + 2]);
+        mb = smax3(mb, sacc[1][v + 1], sacc[0][v + 3]);
       }
-      mx = fmaxf(ma, mb);
+      mx = smax(smax3(ma, mb, sacc[1][14]), sacc[1][15]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c0);
+    {  // the other 32 keys of this query sit in lane ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_new = smax(m_run, mx * c0);
     if (__ballot(m_new > m_run) != 0ull) {   // rescale only when some row max grew
       const float alpha = exp2_hw16(m_run - m_new);
 #pragma unroll

@@ -39,15 +39,6 @@
 namespace rotattn {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-// Maximum of finite values or -inf (the scores and running maxima here): the
-// plain instructions, because fmaxf's NaN rules make the compiler add a
-// canonicalizing max before most two-input maxima (five per key block).
-__device__ __forceinline__ void max3_raw(float& d, float a, float b, float c) {
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-}
-__device__ __forceinline__ void max_raw(float& d, float a, float b) {
-  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-}
 
 // FP6 E2M3 bits (sign, 2 exponent bits with bias 1, 3 mantissa bits) of a
 // 4-bit two's-complement code in [-7, 7]: every such integer is exact in E2M3
@@ -364,16 +355,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     float mx;
     if (!kRagged) {
       // two interleaved max3 chains over the 32 values of this lane
-      float ma, mb;
-      max3_raw(ma, s0[0], s1[0], s0[2]);
-      max3_raw(mb, s0[1], s1[1], s0[3]);
+      float ma = smax3(s0[0], s1[0], s0[2]);
+      float mb = smax3(s0[1], s1[1], s0[3]);
 #pragma unroll
       for (int v = 2; v < 14; v += 2) {
-        max3_raw(ma, ma, s1[v], s0[v + 2]);
-        max3_raw(mb, mb, s1[v + 1], s0[v + 3]);
+        ma = smax3(ma, s1[v], s0[v + 2]);
+        mb = smax3(mb, s1[v + 1], s0[v + 3]);
       }
-      max3_raw(mx, ma, mb, s1[14]);
-      max_raw(mx, mx, s1[15]);
+      mx = smax(smax3(ma, mb, s1[14]), s1[15]);
     } else {
       mx = -INFINITY;
 #pragma unroll
@@ -385,11 +374,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     }
     {  // the other 32 keys of this query sit in lane ^ 32
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      max_raw(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     // max over the block of acc * c = (max acc) * c, as c >= 0 (acc is an exact integer)
-    float m_new;
-    max_raw(m_new, m_run, fmul_rn(mx, cs));
+    const float m_new = smax(m_run, fmul_rn(mx, cs));
     const bool flush = DUMP || __ballot(m_new > m_run) != 0ull;
     if (flush) {
       // alpha = 2^(m_old - m_new): 0 before the first block, 1 where the row max did not grow

@@ -161,6 +161,15 @@ __device__ __forceinline__ uint32_t uniform_word_u(uint64_t base, int i) {
   return *reinterpret_cast<const_u32p>(base + 4ull * (uint64_t)(int64_t)i);
 }
 
+// Maximum for attention scores and running maxima (finite or -inf): the
+// IEEE maximum, which gfx950 computes with v_maximum3_f32 and no extra
+// instructions, where fmaxf's NaN rules make the compiler add a
+// canonicalizing max before most two-input maxima. (A NaN score, possible
+// only from non-finite inputs, propagates.) Nested calls fuse into
+// three-input instructions.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float smax3(float a, float b, float c) { return smax(smax(a, b), c); }
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
