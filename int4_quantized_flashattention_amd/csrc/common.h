@@ -62,31 +62,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
 }
-// Direct-to-LDS copies: lane l's 16 (or 4) bytes at `src` land at LDS byte
-// address m0 + 16 l (or 4 l). Written as inline asm rather than the builtin so
-// that the compiler does not make LDS reads wait for them: once the stage loop
-// wraps around it can no longer tell which stage a builtin copy writes and
-// waits for every copy in flight. The callers order copies and reads with
-// explicit vmcnt waits and barriers. No register output: the copy writes LDS
-// only, and its address registers are read when it issues. M0 is restored.
+// Direct-to-LDS copies (lds_copy16_s / lds_copy4_s below): lane l's 16 (or 4)
+// bytes land at LDS byte address m0 + 16 l (or 4 l). Written as inline asm
+// rather than the builtin so that the compiler does not make LDS reads wait
+// for them: once the stage loop wraps around it can no longer tell which stage
+// a builtin copy writes and waits for every copy in flight. The callers order
+// copies and reads with explicit vmcnt waits and barriers. No register output:
+// the copy writes LDS only, and its address registers are read when it issues.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t m0) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(src)
-      : "memory");
-}
-__device__ __forceinline__ void lds_copy4(const void* src, uint32_t m0) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(src)
-      : "memory");
 }
 
 // A wave-uniform pointer in scalar registers: each 32-bit half goes through
@@ -97,9 +81,9 @@ __device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
   return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
          (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
 }
-// The same copies addressed as a wave-uniform base in scalar registers plus a
-// 32-bit per-lane byte offset: no 64-bit vector address per copy, and M0 is
-// set without saving it (declared clobbered).
+// The copies address a wave-uniform base in scalar registers plus a 32-bit
+// per-lane byte offset (no 64-bit vector address per copy); M0 is set without
+// saving it (declared clobbered).
 __device__ __forceinline__ void lds_copy16_s(uint64_t base, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
@@ -135,16 +119,6 @@ __device__ __forceinline__ uint32_t uniform_byte(const uint8_t* base, int i) {
   typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
   const uint32_t w = *reinterpret_cast<const_u32p>(((uint64_t)hi << 32) | (lo & ~3u));
   return (w >> (8 * (lo & 3u))) & 0xFFu;
-}
-
-// Word i of a uint32 array that no thread writes during the kernel, for a
-// wave-uniform base and i, through the scalar unit (see uniform_byte).
-__device__ __forceinline__ uint32_t uniform_word(const uint32_t* base, int i) {
-  const uint64_t addr = reinterpret_cast<uintptr_t>(base + i);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
-  typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
-  return *reinterpret_cast<const_u32p>(((uint64_t)hi << 32) | lo);
 }
 
 // The same reads from a base already made uniform by uniform_ptr, with a
