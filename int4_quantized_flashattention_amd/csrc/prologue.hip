@@ -187,60 +187,33 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// Grid (NB, H, 2B): blockIdx.z = 2*b + tensor (0 = Q, 1 = K).
+// Shape of the prologue's work: each token's rotated row (D' values) in
+// 32-value chunks, one chunk per task, one task per thread and round.
 template <int D, int ROT>
-__global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __half* q, const __half* k,
-                                                          const float* tab, QKOut o) {
-  constexpr int DP = (ROT == 1) ? 192 : D;
-  constexpr int N = (ROT == 1) ? 64 : D;       // Walsh-Hadamard size (ROT 2: no Hadamard)
-  constexpr int PARTS = DP / 32;               // 32-value chunks per token
-  constexpr int TASKS = kBlock * PARTS;        // multiple of 64
-  constexpr int ROUNDS = (TASKS + 255) / 256;
-  __shared__ float Y[kBlock][D + 4];
-  __shared__ float red[4];
-  __shared__ int coord[kBlock][3];
+struct ProShape {
+  static constexpr int DP = (ROT == 1) ? 192 : D;
+  static constexpr int N = (ROT == 1) ? 64 : D;       // Walsh-Hadamard size (ROT 2: no Hadamard)
+  static constexpr int PARTS = DP / 32;               // 32-value chunks per token
+  static constexpr int TASKS = kBlock * PARTS;        // multiple of 64
+  static constexpr int ROUNDS = (TASKS + 255) / 256;
+};
 
-  const int blk = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
-  const __half* x = tensor ? k : q;
-
-  load_block_to_lds<D>(kp, x, b, h, blk, Y);
-  rope_lds<D, ROT == 2>(kp, tab, blk, Y, coord);
-  __syncthreads();
-  __half* rcopy = tensor ? o.k_rope : o.q_rope;
-  if (rcopy != nullptr) store_rope_copy<D>(kp, b, h, blk, Y, rcopy);
-  // block sum of the RoPE'd rows over the valid tokens (ascending order), the
-  // representative token of block-sparse attention before its division by the
-  // count (RainFusion2.0, section 3.2)
-  float* bsum = tensor ? o.k_bsum : o.q_bsum;
-  if (bsum != nullptr) {
-    const int n = min(kBlock, kp.L - blk * kBlock);
-    float* dst = bsum + ((long long)(b * kp.H + h) * kp.NB + blk) * D;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-      float acc = 0.f;
-      for (int t = 0; t < n; ++t) acc = fadd_rn(acc, Y[t][d]);
-      dst[d] = acc;
-    }
-  }
-
-  // Walsh-Hadamard on 32-value chunks: stages 1..16 in registers, 32 and 64 across lanes.
-  float v[ROUNDS][32];
+// Rotation, quantization and stores of one 64-token block, given the RoPE'd
+// values of each task's chunk in v (task = threadIdx.x + 256 r = token * PARTS
+// + chunk): the Walsh-Hadamard on 32-value chunks (stages 1..16 in registers,
+// 32 and 64 across lanes), the block scale, the codes, the scale and the error
+// flag. Called by the whole workgroup.
+template <int D, int ROT>
+__device__ __forceinline__ void rotate_quantize(const KProblem& kp, const QKOut& o, int b, int h, int blk,
+                                                int tensor, float (&v)[ProShape<D, ROT>::ROUNDS][32], float* red) {
+  using S = ProShape<D, ROT>;
+  constexpr int DP = S::DP, N = S::N, PARTS = S::PARTS, TASKS = S::TASKS, ROUNDS = S::ROUNDS;
   float amax = 0.f;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int task = threadIdx.x + 256 * r;
     if (task < TASKS) {  // wave-uniform
-      const int tok = task / PARTS, part = task - (task / PARTS) * PARTS;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int p = 32 * part + e;
-        if (ROT == 1) {
-          const int g = p >> 6, oo = p & 63;
-          v[r][e] = (oo < kp.split[g]) ? Y[tok][kp.off[g] + oo] : 0.f;
-        } else {
-          v[r][e] = Y[tok][p];
-        }
-      }
+      const int part = task - (task / PARTS) * PARTS;
       if constexpr (ROT != 2) {
 #pragma unroll
       for (int hs = 1; hs < 32; hs <<= 1) {
@@ -289,24 +262,26 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
       // divisions sit behind a wave-uniform branch taken only when some lane
       // of the wave has such a value (otherwise the compiler evaluates them
       // for every element and selects).
-      float qd[32];
+      // A value is near a half-integer when it is more than 0.5 - 1e-6 from
+      // its nearest integer (qd - rint(qd) is exact). No clamp to [-7, 7] is
+      // needed: |x| <= amax, so |x * float(1/s)| <= 7 (1 + 3 2^-24) < 7.5 and
+      // the exact quotient is at most 7.
+      float qd[32], cq[32];
       bool near_tie = false;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         qd[j] = fmul_rn(v[r][j], rs);
-        const float fr = qd[j] - floorf(qd[j]);
-        near_tie |= fabsf(fr - 0.5f) < 1e-6f;
+        cq[j] = rintf(qd[j]);
+        near_tie |= fabsf(qd[j] - cq[j]) > 0.5f - 1e-6f;
       }
       if (__builtin_amdgcn_ballot_w64(near_tie && s != 0.f) != 0ull) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const float fr = qd[j] - floorf(qd[j]);
-          if (s != 0.f && fabsf(fr - 0.5f) < 1e-6f) qd[j] = fdiv_rn(v[r][j], s);
-        }
+        for (int j = 0; j < 32; ++j)
+          if (s != 0.f && fabsf(qd[j] - cq[j]) > 0.5f - 1e-6f) cq[j] = rintf(fdiv_rn(v[r][j], s));
       }
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        const float c = (s != 0.f) ? fminf(fmaxf(rintf(qd[j]), -7.f), 7.f) : 0.f;
+        const float c = (s != 0.f) ? cq[j] : 0.f;
         const float e = fsub_rn(v[r][j], fmul_rn(s, c));
         se += e * e;
         sx += v[r][j] * v[r][j];
@@ -328,6 +303,146 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
     (tensor ? o.k_flag : o.q_flag)[bi] = flag;
     if (tensor == 1 && flag) atomicOr(&o.head_kflag[b * kp.H + h], 1u);
   }
+}
+
+
+// Grid (NB, H, 2B): blockIdx.z = 2*b + tensor (0 = Q, 1 = K). The block is
+// staged in LDS (RoPE thread per pair, rotation thread per chunk); this
+// kernel also writes the RoPE'd copies and the block sums when asked.
+template <int D, int ROT>
+__global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __half* q, const __half* k,
+                                                          const float* tab, QKOut o) {
+  using S = ProShape<D, ROT>;
+  constexpr int PARTS = S::PARTS, TASKS = S::TASKS, ROUNDS = S::ROUNDS;
+  __shared__ float Y[kBlock][D + 4];
+  __shared__ float red[4];
+  __shared__ int coord[kBlock][3];
+
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
+  const __half* x = tensor ? k : q;
+
+  load_block_to_lds<D>(kp, x, b, h, blk, Y);
+  rope_lds<D, ROT == 2>(kp, tab, blk, Y, coord);
+  __syncthreads();
+  __half* rcopy = tensor ? o.k_rope : o.q_rope;
+  if (rcopy != nullptr) store_rope_copy<D>(kp, b, h, blk, Y, rcopy);
+  // block sum of the RoPE'd rows over the valid tokens (ascending order), the
+  // representative token of block-sparse attention before its division by the
+  // count (RainFusion2.0, section 3.2)
+  float* bsum = tensor ? o.k_bsum : o.q_bsum;
+  if (bsum != nullptr) {
+    const int n = min(kBlock, kp.L - blk * kBlock);
+    float* dst = bsum + ((long long)(b * kp.H + h) * kp.NB + blk) * D;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      float acc = 0.f;
+      for (int t = 0; t < n; ++t) acc = fadd_rn(acc, Y[t][d]);
+      dst[d] = acc;
+    }
+  }
+
+  float v[ROUNDS][32];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int task = threadIdx.x + 256 * r;
+    if (task < TASKS) {  // wave-uniform
+      const int tok = task / PARTS, part = task - (task / PARTS) * PARTS;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int p = 32 * part + e;
+        if (ROT == 1) {
+          const int g = p >> 6, oo = p & 63;
+          v[r][e] = (oo < kp.split[g]) ? Y[tok][kp.off[g] + oo] : 0.f;
+        } else {
+          v[r][e] = Y[tok][p];
+        }
+      }
+    }
+  }
+  rotate_quantize<D, ROT>(kp, o, b, h, blk, tensor, v, red);
+}
+
+// The same without the LDS tile, for the common call (no RoPE'd copies, no
+// block sums) when every RoPE group starts at an even dim and has an even
+// size, so that each pair (2i, 2i + 1) lies inside one 32-value chunk: each
+// thread loads its chunk of one token with 16-byte loads and applies RoPE in
+// registers (the same products and sums, rounded the same way), then the
+// rotation and quantization as above. No LDS beyond the reductions, so the
+// occupancy is set by the registers. ROT 0 (full Hadamard) or 2 (pair
+// rotation folded into RoPE).
+template <int D, int ROT>
+__global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const __half* q, const __half* k,
+                                                              const float* tab, QKOut o) {
+  static_assert(ROT == 0 || ROT == 2, "chunks of the unpadded row");
+  using S = ProShape<D, ROT>;
+  constexpr int PARTS = S::PARTS, TASKS = S::TASKS;
+  static_assert(S::ROUNDS == 1, "one chunk per thread");
+  __shared__ float red[4];
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
+  const __half* x = tensor ? k : q;
+
+  float v[1][32];
+  const int task = threadIdx.x;
+  if (task < TASKS) {  // wave-uniform
+    const int tok = task / PARTS, part = task - tok * PARTS;
+    const int tg = blk * kBlock + tok;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[0][e] = 0.f;
+    if (tg < kp.L) {
+      const __half* src = x + (long long)b * kp.sb + (long long)h * kp.sh + (long long)tg * kp.sl + 32 * part;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 u = reinterpret_cast<const uint4*>(src)[c];
+        const __half* hv = reinterpret_cast<const __half*>(&u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[0][8 * c + e] = __half2float(hv[e]);
+      }
+      // grid coordinates of the token (text tokens: none)
+      const bool text = tg < kp.prefix;
+      int coord[3] = {0, 0, 0};
+      if (!text) {
+        const int idx = tg - kp.prefix, hw = kp.Hh * kp.W;
+        const int t = idx / hw, rem = idx - t * hw;
+        const int hq = rem / kp.W;
+        coord[0] = t;
+        coord[1] = hq;
+        coord[2] = rem - hq * kp.W;
+      }
+      // cos/sin of the chunk's 16 pairs, every table load first (video tokens
+      // only: the tables have no entries for text tokens, and with no video
+      // tokens at all none)
+      float cv[16], sv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        cv[i] = 1.f;
+        sv[i] = 0.f;
+      }
+      if (!text) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d = 32 * part + 2 * i;
+          const int a = (d >= kp.off[1]) + (d >= kp.off[2]);
+          const int pi = (d - kp.off[a]) >> 1;
+          const int pos = a == 0 ? coord[0] : a == 1 ? coord[1] : coord[2];
+          const int npos = a == 0 ? kp.T : a == 1 ? kp.Hh : kp.W;
+          const float* ct = tab + kp.tab_off[a] + pos * kp.npair[a] + pi;
+          cv[i] = ct[0];
+          sv[i] = ct[npos * kp.npair[a]];
+        }
+      }
+      if (!text || ROT == 2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float c = text ? kp.pair_c : cv[i], s = text ? kp.pair_s : sv[i];
+          const float x0 = v[0][2 * i], x1 = v[0][2 * i + 1];
+          v[0][2 * i] = fsub_rn(fmul_rn(x0, c), fmul_rn(x1, s));
+          v[0][2 * i + 1] = fadd_rn(fmul_rn(x0, s), fmul_rn(x1, c));
+        }
+      }
+    }
+  }
+  rotate_quantize<D, ROT>(kp, o, b, h, blk, tensor, v, red);
 }
 
 // RoPE only, into a dense fp16 copy (the input of the whole-call FP16 path).
@@ -357,6 +472,21 @@ hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32
 hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half* k, const float* tab,
                               const QKOut& o, hipStream_t s) {
   dim3 grid(kp.NB, kp.H, 2 * kp.B);
+  bool even_pairs = true;
+  for (int a = 0; a < 3; ++a) even_pairs = even_pairs && kp.off[a] % 2 == 0 && kp.split[a] % 2 == 0;
+  const bool reg_path = even_pairs && kp.rotation != 1 && o.q_rope == nullptr && o.k_rope == nullptr &&
+                        o.q_bsum == nullptr && o.k_bsum == nullptr;
+  if (reg_path) {
+    if (kp.D == 128 && kp.rotation == 0)
+      hipLaunchKernelGGL((qk_prologue_reg_kernel<128, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+    else if (kp.D == 128)
+      hipLaunchKernelGGL((qk_prologue_reg_kernel<128, 2>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+    else if (kp.D == 64 && kp.rotation == 0)
+      hipLaunchKernelGGL((qk_prologue_reg_kernel<64, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+    else
+      hipLaunchKernelGGL((qk_prologue_reg_kernel<64, 2>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+    return hipGetLastError();
+  }
   if (kp.D == 128 && kp.rotation == 0)
     hipLaunchKernelGGL((qk_prologue_kernel<128, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
   else if (kp.D == 128 && kp.rotation == 1)
