@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void v_quant_kernel(KProblem kp, const __half*
                                                       VOut o) {
   constexpr int G = D / 8;
   constexpr int RPP = 256 / G;
-  __shared__ float sv[D];
+  __shared__ float sv[D], rsv[D];
   __shared__ int8_t C[kBlock][D + 4];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * kp.H + h;
@@ -63,30 +63,48 @@ __global__ __launch_bounds__(256) void v_quant_kernel(KProblem kp, const __half*
   if (t < D) {
     const float s = fdiv_rn(__uint_as_float(absmax_bits[bh * D + t]), 7.0f);
     sv[t] = s;
+    rsv[t] = (s != 0.f) ? fdiv_rn(1.0f, s) : 0.f;
     if (blk == 0) o.v_scale[bh * D + t] = s;
   }
   __syncthreads();
   const int g = t % G, r0 = t / G;
   const __half* base = v + (long long)b * kp.sb + (long long)h * kp.sh + g * 8;
+  float s8[8], rs8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s8[e] = sv[g * 8 + e];
+    rs8[e] = rsv[g * 8 + e];
+  }
   for (int r = r0; r < kBlock; r += RPP) {
     const int tok = blk * kBlock + r;
-    int8_t c8[8];
+    float c8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c8[e] = 0.f;
     if (tok < kp.L) {
       const uint4 u = *reinterpret_cast<const uint4*>(base + (long long)tok * kp.sl);
       const __half* hv = reinterpret_cast<const __half*>(&u);
+      // code = rne(x / s) as with IEEE division, from x * float(1/s): that
+      // product is within 8.93e-7 of the rounded quotient (|x / s| <= 7), so
+      // the rounding agrees unless it lies within 1e-6 of a half-integer;
+      // there the division is done exactly, behind a wave-uniform branch. No
+      // clamp is needed: |x| <= absmax, so both quotients round into [-7, 7].
+      float x8[8], q8[8];
+      bool near_tie = false;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float s = sv[g * 8 + e];
-        float c = 0.f;
-        if (s != 0.f) c = fminf(fmaxf(rintf(fdiv_rn(__half2float(hv[e]), s)), -7.f), 7.f);
-        c8[e] = (int8_t)(int)c;
+        x8[e] = __half2float(hv[e]);
+        q8[e] = fmul_rn(x8[e], rs8[e]);
+        c8[e] = rintf(q8[e]);
+        near_tie |= s8[e] != 0.f && fabsf(q8[e] - c8[e]) > 0.5f - 1e-6f;
       }
-    } else {
+      if (__builtin_amdgcn_ballot_w64(near_tie) != 0ull) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c8[e] = 0;
+        for (int e = 0; e < 8; ++e)
+          if (s8[e] != 0.f && fabsf(q8[e] - c8[e]) > 0.5f - 1e-6f) c8[e] = rintf(fdiv_rn(x8[e], s8[e]));
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) C[r][g * 8 + e] = c8[e];
+    for (int e = 0; e < 8; ++e) C[r][g * 8 + e] = (int8_t)(int)c8[e];   // a zero scale gives 0 * 0 = 0
   }
   __syncthreads();
   const long long blk_idx = (long long)bh * kp.NB + blk;
