@@ -159,3 +159,37 @@ def test_prologue_rounding_ties():
         codes = G.unpack_qk_codes(G.host(getattr(qk, f"{t}_codes")))[0, 0]
         assert np.array_equal(codes, o[t]["codes"]), t
         assert (np.abs(o[t]["rot"][:, 1:] % 1.0 - 0.5) < 1e-12).all()   # every rotated value but dim 0 is a tie
+
+
+def test_vquant_rounding_ties():
+    """V values on exact half-integers of the quantization step: each channel holds one token at 7 (s = 1)
+    and the rest in {+-0.5, +-1.5, ..., +-6.5}, exact in fp16, so every code but the 7s is a rounding tie
+    that must go to even, as in the oracle; an all-zero channel gets scale 0 and codes 0."""
+    G.require_gpu()
+    w = W.WORKLOADS["tiny"].replace(H=1, grid=(1, 5, 30))   # L = 150: two full key blocks and a ragged one
+    L, D = w.L, w.D
+    rng = np.random.default_rng(78)
+    halves = np.arange(-6.5, 7.0, 1.0)
+    y = rng.choice(halves, size=(L, D))
+    y[rng.integers(0, L, size=D), np.arange(D)] = 7.0          # absmax 7 in every channel
+    y[:, 5] = 0.0                                              # one all-zero channel
+    v = y.astype(np.float16)[None, None]
+    assert np.array_equal(v[0, 0].astype(np.float64), y)
+    x = {"q": rng.standard_normal((1, 1, L, D)).astype(np.float16),
+         "k": rng.standard_normal((1, 1, L, D)).astype(np.float16), "v": v}
+    p = G.R.problem_from_workload(w)
+    vq = G.R.rotattn_quantize_v(p, G.dev(x["v"]))
+    o = G.oracle_head(w, x, 0, 0)
+    scale = G.host(vq.v_scale)[0, 0]
+    want_scale = np.ones(D, np.float32)
+    want_scale[5] = 0.0
+    assert np.array_equal(scale, want_scale)
+    assert np.array_equal(scale, o["v_scale"])
+    codes = G.decode_v_codes(G.host(vq.v_codes))[0, 0]
+    assert np.array_equal(codes, o["v_codes"])
+    assert np.array_equal(G.host(vq.v_colsum)[0, 0], o["v_colsum"])
+    # the ties really are ties, and they went to even
+    c = o["v_codes"][:L].astype(np.float64)
+    tie = np.abs(y % 1.0 - 0.5) < 1e-12
+    assert tie.sum() > L * D // 2
+    assert (c[tie] % 2 == 0).all()
