@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
 constexpr int kFp6 = 2;
 
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
-// 64, the block's LDS image (FP6 K rows, FP6 V^T rows, the K scale) arrives in
+// 64, the block's LDS image (FP6 K rows, FP6 V^T rows) arrives in
 // one stage of an NST-stage ring through direct-to-LDS loads issued NST - 1
 // blocks ahead; one barrier per block. Every wave computes S^T of its 32
 // queries (FP6 products), the online softmax and P codes in registers, and
@@ -136,31 +136,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   constexpr int KST = kv_kst(DP);
   constexpr int IMG = kv_image_bytes(DP, DV);   // one LDS stage = one block's image
   constexpr int NDMA = IMG / (NT * 16);    // 16-byte direct-to-LDS loads per thread per block
-  constexpr int NVM = NDMA + 1;            // vector-memory instructions per wave per block (+ the K scale)
+  constexpr int NVM = NDMA;                // vector-memory instructions per wave per block
   static_assert(IMG % (NT * 16) == 0, "a stage must split evenly over the workgroup");
   static_assert(NST == 3 || NST == 4, "three or four LDS stages");
   // One LDS array per stage, always indexed by a compile-time stage number:
   // the compiler then knows that reads of one stage cannot alias the
   // direct-to-LDS copies into another and does not wait for those copies.
-  // Each stage has a 64-float slot that receives the block's K scale.
   __shared__ __attribute__((aligned(16))) uint8_t stg0[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t stg1[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t stg2[IMG];
   __shared__ __attribute__((aligned(16))) uint8_t stg3[NST == 4 ? IMG : 16];
-  __shared__ float ksc0[64], ksc1[64], ksc2[64], ksc3[64];
   auto stage = [&](auto s_tag) __attribute__((always_inline)) -> uint8_t* {
     constexpr int S = decltype(s_tag)::value;
     if constexpr (S == 0) return stg0;
     else if constexpr (S == 1) return stg1;
     else if constexpr (S == 2) return stg2;
     else return stg3;
-  };
-  auto kscale_slot = [&](auto s_tag) __attribute__((always_inline)) -> float* {
-    constexpr int S = decltype(s_tag)::value;
-    if constexpr (S == 0) return ksc0;
-    else if constexpr (S == 1) return ksc1;
-    else if constexpr (S == 2) return ksc2;
-    else return ksc3;
   };
 
   const int tid = threadIdx.x;
@@ -266,10 +257,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint8_t* img = a.kv_image + (long long)bh * NB * IMG;   // wave-uniform
   const int toff = tid * 16;                                     // this thread's piece of every round
-  // The K block scale follows in one 4-byte copy per lane (every lane of every
-  // wave copies the same value into the stage's scale slot; no branch, so the
-  // compiler keeps the copy's stage static), so that every wave issues NVM
-  // vector-memory instructions per block.
+  // The block's K scale is read through the scalar unit when it is needed.
   const float* kscale = a.k_scale + (long long)bh * NB;
   // Per-thread byte offsets of the pieces stay in registers for the whole
   // loop; the block's image base goes in scalar registers.
@@ -282,7 +270,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     const uint32_t dst = lds_addr(stage(s_tag)) + wave_u * 1024;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) lds_copy16_s(src, voffs[i], dst + i * NT * 16);
-    lds_copy4_s(ksc_s + 4ull * (uint64_t)j, 0u, lds_addr(kscale_slot(s_tag)));
   };
 
   // O^T accumulates on the FP6 matrix path in float32. The V codes are E2M3
@@ -345,11 +332,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   };
 
   // Row max, rescale, P codes and P.V of block j (its S^T is in s0/s1, its V in `stage`).
-  auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, const float* ksc, int j) __attribute__((always_inline)) {
+  auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, int j) __attribute__((always_inline)) {
     constexpr bool kRagged = decltype(ragged_tag)::value;
     const uint8_t* Vs = Ks + KST;
     // c = float(float(sq c0) sk)
-    const float sk = ksc[0];
+    // the block's K scale through the scalar unit (uniform address)
+    typedef const __attribute__((address_space(4))) float* const_f32p;
+    const float sk = *reinterpret_cast<const_f32p>(ksc_s + 4ull * (uint64_t)j);
     const float cs = fmul_rn(cq, sk);
     const int key0 = j * kBlock;
     float mx;
@@ -513,7 +502,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
     if (work) {
       // S^T of the next block after this block's P.V (stale data when there
       // is no next block: computed, never used)
-      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), kscale_slot(s_tag), q[0]);
+      softmax_pv(std::integral_constant<bool, false>(), stage(s_tag), q[0]);
       qk(stage(S1()), s0, s1);
       __builtin_amdgcn_s_setprio(0);
     }
@@ -542,8 +531,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   if (j < NB && work) {
     wait_vmcnt<0>();
     const uint8_t* Ks = st == 0 ? stage(I0()) : st == 1 ? stage(I1()) : st == 2 ? stage(I2()) : stage(I3());
-    const float* ksc = st == 0 ? ksc0 : st == 1 ? ksc1 : st == 2 ? ksc2 : ksc3;
-    softmax_pv(std::integral_constant<bool, true>(), Ks, ksc, j);
+    softmax_pv(std::integral_constant<bool, true>(), Ks, j);
   }
 
   if (DUMP || !work) return;

@@ -62,8 +62,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
 }
-// Direct-to-LDS copies (lds_copy16_s / lds_copy4_s below): lane l's 16 (or 4)
-// bytes land at LDS byte address m0 + 16 l (or 4 l). Written as inline asm
+// Direct-to-LDS copies (lds_copy16_s below): lane l's 16 bytes land at LDS
+// byte address m0 + 16 l. Written as inline asm
 // rather than the builtin so that the compiler does not make LDS reads wait
 // for them: once the stage loop wraps around it can no longer tell which stage
 // a builtin copy writes and waits for every copy in flight. The callers order
@@ -86,12 +86,6 @@ __device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
 // saving it (declared clobbered).
 __device__ __forceinline__ void lds_copy16_s(uint64_t base, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(base)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_copy4_s(uint64_t base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(base)
                : "memory", "m0");
