@@ -102,15 +102,25 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
     const int r = o / QROW, c = (o - r * QROW) / 8, x = kv_swz(DP, r);   // c: first of the slot's two pieces
     uint32_t f6[6];
     e2m3_pack32(*reinterpret_cast<const uint4*>(kg + o), f6);
-    *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-    *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
+    if constexpr (kv_dense(DP, DV)) {
+      *reinterpret_cast<uint4*>(dst + kvd_ka(r, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+      *reinterpret_cast<uint2*>(dst + kvd_kb(r, c / 2)) = make_uint2(f6[4], f6[5]);
+    } else {
+      *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+      *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
+    }
   }
   for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16) {
     const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);   // c = 2 hh
     uint32_t f6[6];
     e2m3_pack32_v(*reinterpret_cast<const uint4*>(vg + o), f6);
-    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-    *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
+    if constexpr (kv_dense(DP, DV)) {
+      *reinterpret_cast<uint4*>(dst + kvd_va(ch, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+      *reinterpret_cast<uint2*>(dst + kvd_vb(ch, c / 2)) = make_uint2(f6[4], f6[5]);
+    } else {
+      *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+      *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
+    }
   }
 }
 
@@ -289,27 +299,43 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   // same permutation) at logical pieces 4c + 2hh and 4c + 2hh + 1 (dims
   // [64 c + 32 hh, +32)); V channel row ct*32 + col (the same permutation for
   // every ct) at logical piece 2*hh + s.
-  int koff[2 * NC], voff[2];
+  // kA/kB: the 16- and 8-byte parts of K row col's slot for slice c; row
+  // col + 32 lies dKA further (its 8-byte part at kB1); vA/vB: V channel row
+  // col's slot, tile ct at vA + ct dVA and vB[ct]. All offsets from the stage.
+  constexpr bool kDense = kv_dense(DP, DV);
+  constexpr int dKA = kDense ? 2048 : 32 * DP;
+  constexpr int dVA = kDense ? 1024 : 32 * 64;
+  int kA[NC], kB[NC], kB1[NC], vA, vB[NCT];
+  if constexpr (kDense) {
 #pragma unroll
-  for (int c = 0; c < 2 * NC; ++c) koff[c] = col * DP + 16 * ((4 * (c >> 1) + 2 * hh + (c & 1)) ^ kv_swz(DP, col));
+    for (int c = 0; c < NC; ++c) {
+      kA[c] = kvd_ka(col, 2 * c + hh);
+      kB[c] = kvd_kb(col, 2 * c + hh);
+      kB1[c] = kB[c] + 1024;
+    }
+    vA = kvd_va(col, hh);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) voff[s] = col * 64 + 16 * ((2 * hh + s) ^ kv_swz(64, col));
+    for (int ct = 0; ct < NCT; ++ct) vB[ct] = kvd_vb(col, hh) + ct * 512;
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kA[c] = col * DP + 16 * ((4 * c + 2 * hh) ^ kv_swz(DP, col));
+      kB[c] = col * DP + 16 * ((4 * c + 2 * hh + 1) ^ kv_swz(DP, col));
+      kB1[c] = kB[c] + 32 * DP;
+    }
+    vA = KST + col * 64 + 16 * ((2 * hh) ^ kv_swz(64, col));
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) vB[ct] = KST + col * 64 + 16 * ((2 * hh + 1) ^ kv_swz(64, col)) + ct * 32 * 64;
+  }
   // Each operand is a 16-byte and an 8-byte LDS read that must land in six
   // consecutive registers. Two 8-byte reads from one base register get paired
   // into a single read2 instruction, which then needs register moves; an
   // opaque base register of its own for every 8-byte read (of K row col + 32
   // and of each V tile) keeps them apart.
-  int khi[NC], vhi[NCT];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    khi[c] = koff[2 * c + 1] + 32 * DP;
-    asm volatile("" : "+v"(khi[c]));
-  }
+  for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(kB1[c]));
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    vhi[ct] = voff[1] + ct * 32 * 64;
-    if (ct > 0) asm volatile("" : "+v"(vhi[ct]));
-  }
+  for (int ct = 1; ct < NCT; ++ct) asm volatile("" : "+v"(vB[ct]));
 
   // S^T of the block in `stage` (the integer q.k as exact floats), as two
   // 32-key halves, on the FP6 matrix path (E2M3 codes, no block scaling)
@@ -320,10 +346,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       // the 24 bytes of the slot: a full first piece and half of the second
-      const v4i a0l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c]);
-      const v2i a0h = *reinterpret_cast<const v2i*>(Ks + koff[2 * c + 1]);
-      const v4i a1l = *reinterpret_cast<const v4i*>(Ks + koff[2 * c] + 32 * DP);
-      const v2i a1h = *reinterpret_cast<const v2i*>(Ks + khi[c]);
+      const v4i a0l = *reinterpret_cast<const v4i*>(Ks + kA[c]);
+      const v2i a0h = *reinterpret_cast<const v2i*>(Ks + kB[c]);
+      const v4i a1l = *reinterpret_cast<const v4i*>(Ks + kA[c] + dKA);
+      const v2i a1h = *reinterpret_cast<const v2i*>(Ks + kB1[c]);
       const v8i a0 = v8i{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], 0, 0};
       const v8i a1 = v8i{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], 0, 0};
       d0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[c], d0, kFp6, kFp6, 0, 0, 0, 0);
@@ -334,7 +360,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   // Row max, rescale, P codes and P.V of block j (its S^T is in s0/s1, its V in `stage`).
   auto softmax_pv = [&](auto ragged_tag, const uint8_t* Ks, int j) __attribute__((always_inline)) {
     constexpr bool kRagged = decltype(ragged_tag)::value;
-    const uint8_t* Vs = Ks + KST;
     // c = float(float(sq c0) sk)
     // the block's K scale through the scalar unit (uniform address)
     typedef const __attribute__((address_space(4))) float* const_f32p;
@@ -443,8 +468,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       // the 24 bytes of channel row ct * 32 + col's slot for this lane half
-      const v4i vl = *reinterpret_cast<const v4i*>(Vs + ct * 32 * 64 + voff[0]);
-      const v2i vh = *reinterpret_cast<const v2i*>(Vs + vhi[ct]);
+      const v4i vl = *reinterpret_cast<const v4i*>(Ks + vA + ct * dVA);
+      const v2i vh = *reinterpret_cast<const v2i*>(Ks + vB[ct]);
       const v8i va = v8i{vl[0], vl[1], vl[2], vl[3], vh[0], vh[1], 0, 0};
       if constexpr (DUMP) {
         // this block's sum alone, to expose the integers sum (pq + 8) v
@@ -579,17 +604,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 // Launch shape per rotated head dim. Four waves per workgroup (32 query rows
 // each), so that independent workgroups share a CU and one's softmax overlaps
 // another's matrix work. Workgroups per CU (kOcc): three at D' = 128, where the
-// registers (at most 168 per lane; the few that spill are epilogue-only
-// pointers) and three three-stage LDS rings fit, which measured 10% faster
-// than two workgroups with four stages and the next block's S^T issued early;
-// two elsewhere (the D' = 192 rings do not fit three times; D = 64 reaches four
-// workgroups per CU through its register count anyway). Stages: as many as
-// kOcc rings fit in the 160 KB of LDS, three or four.
+// registers (at most 168 per lane) and three LDS rings fit, which measured 10%
+// faster than two workgroups with four stages and the next block's S^T issued
+// early; two elsewhere (the D' = 192 rings do not fit three times; D = 64
+// reaches four workgroups per CU through its register count anyway). Stages:
+// three with the dense 12 KB image of D' = D = 128 (four fit, but measured 0.6%
+// slower), else as many as kOcc rings fit in the 160 KB of LDS, three or four.
 template <int DP, int DV>
 struct Shape {
   static constexpr int kWaves = 4;
   static constexpr int kOcc = (DP == 128) ? 3 : 2;
-  static constexpr int kStages = (kOcc * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3;
+  static constexpr int kStages =
+      kv_dense(DP, DV) ? 3 : ((kOcc * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3);
 };
 
 template <int DP, int DV, bool SPARSE>

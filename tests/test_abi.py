@@ -63,9 +63,9 @@ def test_sizes_720p():
     assert s.v_colsum_bytes == 40 * 1182 * 128 * 4
     p2 = Bd.problem_from_workload(W.WORKLOADS["480p"])
     assert Bd.get_sizes(p2).Dp == 192
-    # the attention workspace holds one 16384-byte int8 LDS image per (head, key block): 64 K rows of
-    # 128 bytes and 128 V rows of 64 bytes
-    img = 40 * 1182 * 16384
+    # the attention workspace holds one LDS image per (head, key block): at D' = D = 128 the dense
+    # 12288-byte form (64 K rows and 128 V rows of 24-byte FP6 slots, 4 and 2 slots per row)
+    img = 40 * 1182 * 12288
     vt = 40 * 1182 * 64 * 128 * 2   # transposed fp16 V blocks of the FP16 path
     assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img + vt
     assert Bd.workspace_bytes(p, Bd.CALL_DEBUG_DUMP) == img
