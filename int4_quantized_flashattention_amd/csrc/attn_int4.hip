@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
     uint32_t f6[6];
     e2m3_pack32(*reinterpret_cast<const uint4*>(kg + o), f6);
     if constexpr (kv_dense(DP, DV)) {
-      *reinterpret_cast<uint4*>(dst + kvd_ka(r, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint2*>(dst + kvd_kb(r, c / 2)) = make_uint2(f6[4], f6[5]);
+      *reinterpret_cast<uint4*>(dst + kvd_ka(DP, r, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+      *reinterpret_cast<uint2*>(dst + kvd_kb(DP, r, c / 2)) = make_uint2(f6[4], f6[5]);
     } else {
       *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
       *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
     uint32_t f6[6];
     e2m3_pack32_v(*reinterpret_cast<const uint4*>(vg + o), f6);
     if constexpr (kv_dense(DP, DV)) {
-      *reinterpret_cast<uint4*>(dst + kvd_va(ch, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint2*>(dst + kvd_vb(ch, c / 2)) = make_uint2(f6[4], f6[5]);
+      *reinterpret_cast<uint4*>(dst + kvd_va(DP, ch, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+      *reinterpret_cast<uint2*>(dst + kvd_vb(DP, DV, ch, c / 2)) = make_uint2(f6[4], f6[5]);
     } else {
       *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
       *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
@@ -303,19 +303,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   // col + 32 lies dKA further (its 8-byte part at kB1); vA/vB: V channel row
   // col's slot, tile ct at vA + ct dVA and vB[ct]. All offsets from the stage.
   constexpr bool kDense = kv_dense(DP, DV);
-  constexpr int dKA = kDense ? 2048 : 32 * DP;
+  constexpr int dKA = kDense ? 32 * (DP / 32) * 16 : 32 * DP;
   constexpr int dVA = kDense ? 1024 : 32 * 64;
   int kA[NC], kB[NC], kB1[NC], vA, vB[NCT];
   if constexpr (kDense) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kA[c] = kvd_ka(col, 2 * c + hh);
-      kB[c] = kvd_kb(col, 2 * c + hh);
-      kB1[c] = kB[c] + 1024;
+      kA[c] = kvd_ka(DP, col, 2 * c + hh);
+      kB[c] = kvd_kb(DP, col, 2 * c + hh);
+      kB1[c] = kB[c] + 32 * (DP / 32) * 8;
     }
-    vA = kvd_va(col, hh);
+    vA = kvd_va(DP, col, hh);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) vB[ct] = kvd_vb(col, hh) + ct * 512;
+    for (int ct = 0; ct < NCT; ++ct) vB[ct] = kvd_vb(DP, DV, col, hh) + ct * 512;
   } else {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {

@@ -47,24 +47,34 @@ __device__ __forceinline__ float fdiv_rn(float a, float b) { return __fdiv_rn(a,
 // a multiple of 4096 bytes, so each thread of a 256-thread workgroup copies the
 // same number of 16-byte pieces.
 //
-// At D' = D = 128 the image is dense instead (12288 bytes, no unused bytes):
-// each 24-byte operand slot is split into its first 16 bytes, in a plane of
-// 16-byte entries, and its last 8, in a plane of 8-byte entries. K slot s of
-// key row r (dims [32 s, +32)) and V slot hh of channel row ch (the 32 keys
-// of lane half hh) sit at the kvd_* offsets below; the XOR terms put 16 (32)
-// consecutive rows read at the same slot by a 16-byte (8-byte) read in
-// distinct banks of the 64 (16 lanes of a 16-byte read, or 32 of an 8-byte
-// read, per LDS cycle), and rows 32 apart (tiles of 32 channels) at a
-// constant distance.
-__host__ __device__ constexpr bool kv_dense(int DP, int DV) { return DP == 128 && DV == 128; }
+// With D = 128 (D' = 128 or 192) the image is dense instead (64 K rows of
+// D'/32 slots and D V rows of 2 slots, 24 bytes each: 12288 or 15360 bytes,
+// the latter padded to 16384 for the copy): each 24-byte operand slot is split
+// into its first 16 bytes, in a plane of 16-byte entries, and its last 8, in a
+// plane of 8-byte entries. K slot s of key row r (dims [32 s, +32)) and V slot
+// hh of channel row ch (the 32 keys of lane half hh) sit at the kvd_* offsets
+// below. The slot permutations put the 16 (32) rows that one 16-byte (8-byte)
+// read serves per LDS cycle in distinct banks of the 64 (an XOR with four
+// slots per row, a rotation by one every 8 or 16 rows with six), and keep rows
+// 32 apart (tiles of 32 channels) at a constant distance.
+__host__ __device__ constexpr bool kv_dense(int DP, int DV) { return DV == 128 && (DP == 128 || DP == 192); }
 __host__ __device__ constexpr int kv_kst(int DP) { return kBlock * DP; }
 __host__ __device__ constexpr int kv_image_bytes(int DP, int DV) {
-  return kv_dense(DP, DV) ? (kBlock * DP + DV * 64) * 3 / 4 : kBlock * DP + DV * 64;
+  return kv_dense(DP, DV) ? (kBlock * (DP / 32) * 24 + DV * 48 + 4095) / 4096 * 4096 : kBlock * DP + DV * 64;
 }
-__host__ __device__ constexpr int kvd_ka(int r, int s) { return (r * 4 + (s ^ ((r >> 2) & 3))) * 16; }
-__host__ __device__ constexpr int kvd_kb(int r, int s) { return 4096 + (r * 4 + (s ^ ((r >> 3) & 3))) * 8; }
-__host__ __device__ constexpr int kvd_va(int ch, int hh) { return 6144 + (ch * 2 + (hh ^ ((ch >> 3) & 1))) * 16; }
-__host__ __device__ constexpr int kvd_vb(int ch, int hh) { return 10240 + (ch * 2 + (hh ^ ((ch >> 4) & 1))) * 8; }
+__host__ __device__ constexpr int kvd_ka(int DP, int r, int s) {
+  return (r * (DP / 32) + (DP == 128 ? (s ^ ((r >> 2) & 3)) : (s + ((r >> 3) & 1)) % (DP / 32))) * 16;
+}
+__host__ __device__ constexpr int kvd_kb(int DP, int r, int s) {
+  return kBlock * (DP / 32) * 16 +
+         (r * (DP / 32) + (DP == 128 ? (s ^ ((r >> 3) & 3)) : (s + ((r >> 4) & 1)) % (DP / 32))) * 8;
+}
+__host__ __device__ constexpr int kvd_va(int DP, int ch, int hh) {
+  return kBlock * (DP / 32) * 24 + (ch * 2 + (hh ^ ((ch >> 3) & 1))) * 16;
+}
+__host__ __device__ constexpr int kvd_vb(int DP, int DV, int ch, int hh) {
+  return kBlock * (DP / 32) * 24 + DV * 32 + (ch * 2 + (hh ^ ((ch >> 4) & 1))) * 8;
+}
 // physical piece of logical 16-byte piece c in row r: c ^ kv_swz(row bytes, r)
 __host__ __device__ constexpr int kv_swz(int row_bytes, int r) {
   return row_bytes == 128 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));

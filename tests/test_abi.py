@@ -75,7 +75,7 @@ def test_sizes_720p():
     assert s.bsum_bytes == 40 * 1182 * 128 * 4
     # partial buffers on top only when block routing is on
     pm = Bd.problem_from_workload(W.WORKLOADS["mixed"])
-    img_m = 12 * 512 * 20480   # D' = 192: 64 x 192 + 128 x 64
+    img_m = 12 * 512 * 16384   # D' = 192: dense, 64 x 6 + 128 x 2 slots of 24 bytes (15360), padded to 16384
     assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) >= img_m + 12 * 512 * 64 * 128 * 2 + 12 * 32768 * 128 * 4
 
 
