@@ -83,15 +83,15 @@ __device__ __forceinline__ void e2m3_pack32_v(uint4 p, uint32_t (&o)[6]) {
 }
 
 // Expands one (b, h, key block) into the LDS image the attention kernel copies:
-// the packed K codes of its 64 keys become FP6 E2M3 operands (each run of 32
-// dims in a 32-byte slot: 24 bytes of packed values, 8 unused), and the V
-// codes of each channel FP6 operands in the same slots (32 keys per slot, in
-// the element order of the P operand), all at their permuted LDS offsets.
+// the packed K codes of its 64 keys become FP6 E2M3 operand slots (one per run
+// of 32 dims) and the V codes of each channel two slots (32 keys each, in the
+// element order of the P operand), each slot split over the 16- and 8-byte
+// planes at its kvd_* offsets.
 template <int DP, int DV>
 __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_t* __restrict__ k_codes,
                                                        const uint8_t* __restrict__ v_codes, uint8_t* image) {
   constexpr int QROW = DP / 2, KPK = kBlock * DP / 2, VPK = DV * 32;
-  constexpr int KST = kv_kst(DP), IMG = kv_image_bytes(DP, DV);
+  constexpr int IMG = kv_image_bytes(DP, DV);
   const long long u = blockIdx.x;   // (b * H + h) * NB + block
   const long long bh = u / kp.NB;
   const int j = (int)(u - bh * kp.NB);
@@ -99,28 +99,18 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
   const uint8_t* kg = k_codes + (bh * kp.Lp + (long long)j * kBlock) * QROW;
   const uint8_t* vg = v_codes + u * VPK;
   for (int o = threadIdx.x * 16; o < KPK; o += 256 * 16) {
-    const int r = o / QROW, c = (o - r * QROW) / 8, x = kv_swz(DP, r);   // c: first of the slot's two pieces
+    const int r = o / QROW, sl = (o - r * QROW) / 16;   // key row, slot
     uint32_t f6[6];
     e2m3_pack32(*reinterpret_cast<const uint4*>(kg + o), f6);
-    if constexpr (kv_dense(DP, DV)) {
-      *reinterpret_cast<uint4*>(dst + kvd_ka(DP, r, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint2*>(dst + kvd_kb(DP, r, c / 2)) = make_uint2(f6[4], f6[5]);
-    } else {
-      *reinterpret_cast<uint4*>(dst + r * DP + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint4*>(dst + r * DP + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
-    }
+    *reinterpret_cast<uint4*>(dst + kvd_ka(DP, r, sl)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+    *reinterpret_cast<uint2*>(dst + kvd_kb(DP, r, sl)) = make_uint2(f6[4], f6[5]);
   }
   for (int o = threadIdx.x * 16; o < VPK; o += 256 * 16) {
-    const int ch = o >> 5, c = (o & 31) / 8, x = kv_swz(64, ch);   // c = 2 hh
+    const int ch = o >> 5, hh = (o & 31) / 16;   // channel row, lane half
     uint32_t f6[6];
     e2m3_pack32_v(*reinterpret_cast<const uint4*>(vg + o), f6);
-    if constexpr (kv_dense(DP, DV)) {
-      *reinterpret_cast<uint4*>(dst + kvd_va(DP, ch, c / 2)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint2*>(dst + kvd_vb(DP, DV, ch, c / 2)) = make_uint2(f6[4], f6[5]);
-    } else {
-      *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * (c ^ x)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
-      *reinterpret_cast<uint4*>(dst + KST + ch * 64 + 16 * ((c + 1) ^ x)) = make_uint4(f6[4], f6[5], 0u, 0u);
-    }
+    *reinterpret_cast<uint4*>(dst + kvd_va(DP, ch, hh)) = make_uint4(f6[0], f6[1], f6[2], f6[3]);
+    *reinterpret_cast<uint2*>(dst + kvd_vb(DP, DV, ch, hh)) = make_uint2(f6[4], f6[5]);
   }
 }
 
@@ -143,7 +133,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP6 product each)
   constexpr int NCT = DV / 32;             // 32-channel output tiles
   constexpr int QROW = DP / 2;             // packed code bytes per token
-  constexpr int KST = kv_kst(DP);
   constexpr int IMG = kv_image_bytes(DP, DV);   // one LDS stage = one block's image
   constexpr int NDMA = IMG / (NT * 16);    // 16-byte direct-to-LDS loads per thread per block
   constexpr int NVM = NDMA;                // vector-memory instructions per wave per block
@@ -299,34 +288,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   // same permutation) at logical pieces 4c + 2hh and 4c + 2hh + 1 (dims
   // [64 c + 32 hh, +32)); V channel row ct*32 + col (the same permutation for
   // every ct) at logical piece 2*hh + s.
-  // kA/kB: the 16- and 8-byte parts of K row col's slot for slice c; row
-  // col + 32 lies dKA further (its 8-byte part at kB1); vA/vB: V channel row
-  // col's slot, tile ct at vA + ct dVA and vB[ct]. All offsets from the stage.
-  constexpr bool kDense = kv_dense(DP, DV);
-  constexpr int dKA = kDense ? 32 * (DP / 32) * 16 : 32 * DP;
-  constexpr int dVA = kDense ? 1024 : 32 * 64;
+  // kA/kB: the 16- and 8-byte parts of K row col's slot for slice c (row
+  // col + 32 lies dKA further, its 8-byte part at kB1); vA/vB: V channel row
+  // col's slot, tile ct at vA + ct * 1024 and vB[ct]. All from the stage base.
+  constexpr int dKA = 32 * (DP / 32) * 16;
   int kA[NC], kB[NC], kB1[NC], vA, vB[NCT];
-  if constexpr (kDense) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kA[c] = kvd_ka(DP, col, 2 * c + hh);
-      kB[c] = kvd_kb(DP, col, 2 * c + hh);
-      kB1[c] = kB[c] + 32 * (DP / 32) * 8;
-    }
-    vA = kvd_va(DP, col, hh);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) vB[ct] = kvd_vb(DP, DV, col, hh) + ct * 512;
-  } else {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kA[c] = col * DP + 16 * ((4 * c + 2 * hh) ^ kv_swz(DP, col));
-      kB[c] = col * DP + 16 * ((4 * c + 2 * hh + 1) ^ kv_swz(DP, col));
-      kB1[c] = kB[c] + 32 * DP;
-    }
-    vA = KST + col * 64 + 16 * ((2 * hh) ^ kv_swz(64, col));
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) vB[ct] = KST + col * 64 + 16 * ((2 * hh + 1) ^ kv_swz(64, col)) + ct * 32 * 64;
+  for (int c = 0; c < NC; ++c) {
+    kA[c] = kvd_ka(DP, col, 2 * c + hh);
+    kB[c] = kvd_kb(DP, col, 2 * c + hh);
+    kB1[c] = kB[c] + 32 * (DP / 32) * 8;
   }
+  vA = kvd_va(DP, col, hh);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) vB[ct] = kvd_vb(DP, DV, col, hh) + ct * 512;
   // Each operand is a 16-byte and an 8-byte LDS read that must land in six
   // consecutive registers. Two 8-byte reads from one base register get paired
   // into a single read2 instruction, which then needs register moves; an
@@ -468,7 +443,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       // the 24 bytes of channel row ct * 32 + col's slot for this lane half
-      const v4i vl = *reinterpret_cast<const v4i*>(Ks + vA + ct * dVA);
+      const v4i vl = *reinterpret_cast<const v4i*>(Ks + vA + ct * 1024);
       const v2i vh = *reinterpret_cast<const v2i*>(Ks + vB[ct]);
       const v8i va = v8i{vl[0], vl[1], vl[2], vl[3], vh[0], vh[1], 0, 0};
       if constexpr (DUMP) {
@@ -608,14 +583,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
 // faster than two workgroups with four stages and the next block's S^T issued
 // early; two elsewhere (the D' = 192 rings do not fit three times; D = 64
 // reaches four workgroups per CU through its register count anyway). Stages:
-// three with the dense 12 KB image of D' = D = 128 (four fit, but measured 0.6%
-// slower), else as many as kOcc rings fit in the 160 KB of LDS, three or four.
+// three at D = 128 (with the 12 KB image of D' = 128 four fit, but measured
+// 0.6% slower), else as many as kOcc rings fit in the 160 KB of LDS.
 template <int DP, int DV>
 struct Shape {
   static constexpr int kWaves = 4;
   static constexpr int kOcc = (DP == 128) ? 3 : 2;
   static constexpr int kStages =
-      kv_dense(DP, DV) ? 3 : ((kOcc * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3);
+      (DV == 128) ? 3 : ((kOcc * 4 * (kv_image_bytes(DP, DV) + 256) + 1024 <= 160 * 1024) ? 4 : 3);
 };
 
 template <int DP, int DV, bool SPARSE>

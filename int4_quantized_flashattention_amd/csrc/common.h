@@ -39,35 +39,30 @@ __device__ __forceinline__ float fsub_rn(float a, float b) { return __fsub_rn(a,
 __device__ __forceinline__ float fdiv_rn(float a, float b) { return __fdiv_rn(a, b); }
 
 // LDS stage of one 64-key block in the INT4 attention kernel, and the byte image
-// of it in HBM that the kernel copies with direct-to-LDS loads: 64 K rows of DP
-// bytes (FP6 E2M3 operands: each run of 32 dims in a 32-byte slot, 24 bytes of
-// values and 8 unused), then DV V channel rows of two such FP6 slots. Within
-// a row the 16-byte pieces are permuted by kv_swz so that 8 or 16 consecutive
-// rows read at the same logical piece fall in distinct LDS banks. Every size is
-// a multiple of 4096 bytes, so each thread of a 256-thread workgroup copies the
-// same number of 16-byte pieces.
-//
-// With D = 128 (D' = 128 or 192) the image is dense instead (64 K rows of
-// D'/32 slots and D V rows of 2 slots, 24 bytes each: 12288 or 15360 bytes,
-// the latter padded to 16384 for the copy): each 24-byte operand slot is split
-// into its first 16 bytes, in a plane of 16-byte entries, and its last 8, in a
-// plane of 8-byte entries. K slot s of key row r (dims [32 s, +32)) and V slot
-// hh of channel row ch (the 32 keys of lane half hh) sit at the kvd_* offsets
-// below. The slot permutations put the 16 (32) rows that one 16-byte (8-byte)
-// read serves per LDS cycle in distinct banks of the 64 (an XOR with four
-// slots per row, a rotation by one every 8 or 16 rows with six), and keep rows
-// 32 apart (tiles of 32 channels) at a constant distance.
-__host__ __device__ constexpr bool kv_dense(int DP, int DV) { return DV == 128 && (DP == 128 || DP == 192); }
-__host__ __device__ constexpr int kv_kst(int DP) { return kBlock * DP; }
+// of it in HBM that the kernel copies with direct-to-LDS loads: 64 K rows of
+// DP/32 FP6 E2M3 operand slots and DV V channel rows of two slots, 24 bytes of
+// packed values each. Each slot is split into its first 16 bytes, in a plane
+// of 16-byte entries, and its last 8, in a plane of 8-byte entries (the
+// operand is one 16-byte and one 8-byte LDS read). K slot s of key row r (dims
+// [32 s, +32)) and V slot hh of channel row ch (the 32 keys of lane half hh)
+// sit at the kvd_* offsets below. The slot permutations put the 16 (32) rows
+// that one 16-byte (8-byte) read serves per LDS cycle in distinct banks of the
+// 64 (an XOR with a row bit or two for two or four slots per row, a rotation
+// by one every 8 or 16 rows for six), and keep rows 32 apart (tiles of 32
+// channels) at a constant distance. The image is padded to a multiple of 4096
+// bytes, so each thread of a 256-thread workgroup copies the same number of
+// 16-byte pieces.
 __host__ __device__ constexpr int kv_image_bytes(int DP, int DV) {
-  return kv_dense(DP, DV) ? (kBlock * (DP / 32) * 24 + DV * 48 + 4095) / 4096 * 4096 : kBlock * DP + DV * 64;
+  return (kBlock * (DP / 32) * 24 + DV * 48 + 4095) / 4096 * 4096;
 }
-__host__ __device__ constexpr int kvd_ka(int DP, int r, int s) {
-  return (r * (DP / 32) + (DP == 128 ? (s ^ ((r >> 2) & 3)) : (s + ((r >> 3) & 1)) % (DP / 32))) * 16;
+__host__ __device__ constexpr int kvd_perm(int S, int r, int s, int shift) {
+  // shift: 3 for the 16-byte plane, 4 for the 8-byte plane (two or six slots);
+  // four slots use the two row bits above shift - 1
+  return S == 2 ? (s ^ ((r >> shift) & 1)) : S == 4 ? (s ^ ((r >> (shift - 1)) & 3)) : (s + ((r >> shift) & 1)) % S;
 }
+__host__ __device__ constexpr int kvd_ka(int DP, int r, int s) { return (r * (DP / 32) + kvd_perm(DP / 32, r, s, 3)) * 16; }
 __host__ __device__ constexpr int kvd_kb(int DP, int r, int s) {
-  return kBlock * (DP / 32) * 16 +
-         (r * (DP / 32) + (DP == 128 ? (s ^ ((r >> 3) & 3)) : (s + ((r >> 4) & 1)) % (DP / 32))) * 8;
+  return kBlock * (DP / 32) * 16 + (r * (DP / 32) + kvd_perm(DP / 32, r, s, 4)) * 8;
 }
 __host__ __device__ constexpr int kvd_va(int DP, int ch, int hh) {
   return kBlock * (DP / 32) * 24 + (ch * 2 + (hh ^ ((ch >> 3) & 1))) * 16;
