@@ -184,7 +184,7 @@ int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_
  * required (the FP16 path reads them); otherwise they may be NULL.
  * out: device fp16 with the problem's strides (may not alias inputs).
  * Workspace: ROTATTN_CALL_ATTENTION bytes: the K/V block images the INT4
- * kernel copies into LDS (about 2.5x the packed K + V codes), the transposed
+ * kernel copies into LDS (1.5x the packed K + V codes at D' = D = 128), the transposed
  * fp16 V blocks of the FP16 path (L x D fp16 rounded up to whole blocks;
  * written only when the FP16 path runs), plus the partial results of mixed
  * rows when block_err_tau is finite.

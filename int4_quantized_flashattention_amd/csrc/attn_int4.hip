@@ -27,8 +27,11 @@
 //    (integer identity). FP6 on both sides takes half the matrix-core cycles
 //    of FP8. The float accumulator is rescaled in place when a row max grows.
 //  * A pre-pass expands each key block once into the exact LDS image of one
-//    pipeline stage (FP6 K rows, FP6 V^T rows); the loop copies images into
-//    LDS with direct-to-LDS loads, three or four stages deep.
+//    pipeline stage: every 24-byte FP6 operand slot (32 K codes of one key,
+//    or 32 V codes of one channel) split into a 16-byte and an 8-byte plane,
+//    with slots permuted per row so that the operand reads of a wave meet no
+//    bank twice on the 64-bank LDS. The loop copies images into LDS with
+//    direct-to-LDS loads, three stages deep at D = 128 (four at D = 64).
 //  * Block-sparse instances (RainFusion2.0, section 3.1 mask M) visit only the
 //    key blocks the workgroup's mask row keeps.
 #include "common.h"
@@ -118,8 +121,8 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
 constexpr int kFp6 = 2;
 
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
-// 64, the block's LDS image (FP6 K rows, FP6 V^T rows) arrives in
-// one stage of an NST-stage ring through direct-to-LDS loads issued NST - 1
+// 64, the block's LDS image (FP6 K rows and FP6 V^T rows, each split into
+// 16- and 8-byte planes) arrives in one stage of an NST-stage ring through direct-to-LDS loads issued NST - 1
 // blocks ahead; one barrier per block. Every wave computes S^T of its 32
 // queries (FP6 products), the online softmax and P codes in registers, and
 // O^T on the FP6 matrix path into a float32 accumulator kept at the running
