@@ -159,6 +159,17 @@ __device__ __forceinline__ void store_rope_copy(const KProblem& kp, int b, int h
   }
 }
 
+// floor(n / d) for 0 <= n < 2^22 and 1 <= d <= 2^22: float(n) rcp(d) has a
+// relative error of at most 1.5 ulp, so it is within 3/4 of n / d and its
+// truncation is off by at most one either way; one step each way corrects it
+// (the products fit the 24-bit multiplier)
+__device__ __forceinline__ int quot_small(int n, int d) {
+  int t = (int)((float)n * __builtin_amdgcn_rcpf((float)d));
+  t -= (__mul24(t, d) > n) ? 1 : 0;
+  t += (__mul24(t + 1, d) <= n) ? 1 : 0;
+  return t;
+}
+
 // v of lane ^ MASK (MASK 1 or 2) within the lane's aligned group of four, by
 // a DPP quad permutation (no LDS round trip). The 32-value chunks of one
 // token sit in consecutive lanes from a multiple of PARTS (4, or 2 and 6 with
@@ -281,10 +292,13 @@ __device__ __forceinline__ void rotate_quantize(const KProblem& kp, const QKOut&
       }
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        const float c = (s != 0.f) ? cq[j] : 0.f;
-        const float e = fsub_rn(v[r][j], fmul_rn(s, c));
-        se += e * e;
-        sx += v[r][j] * v[r][j];
+        // (s = 0 only for an all-zero block, whose codes are 0 already)
+        const float c = cq[j];
+        // the error and energy sums with fused multiply-adds: the residual
+        // v - s c is exact, the sums are rounded once per term
+        const float e = __builtin_fmaf(-s, c, v[r][j]);
+        se = __builtin_fmaf(e, e, se);
+        sx = __builtin_fmaf(v[r][j], v[r][j], sx);
         const uint32_t nib = (uint32_t)((int)c) & 0xFu;
         words[j >> 3] |= nib << (4 * (j & 7));
       }
@@ -403,15 +417,28 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const
       int coord[3] = {0, 0, 0};
       if (!text) {
         const int idx = tg - kp.prefix, hw = kp.Hh * kp.W;
-        const int t = idx / hw, rem = idx - t * hw;
-        const int hq = rem / kp.W;
+        int t, hq;
+        if (kp.L <= (1 << 22)) {   // uniform
+          t = quot_small(idx, hw);
+          hq = quot_small(idx - t * hw, kp.W);
+        } else {
+          t = idx / hw;
+          hq = (idx - t * hw) / kp.W;
+        }
         coord[0] = t;
         coord[1] = hq;
-        coord[2] = rem - hq * kp.W;
+        coord[2] = idx - t * hw - hq * kp.W;
       }
       // cos/sin of the chunk's 16 pairs, every table load first (video tokens
       // only: the tables have no entries for text tokens, and with no video
-      // tokens at all none)
+      // tokens at all none). Pair p = 16 part + i of the row (dims 2p, 2p + 1)
+      // lies in axis a = [p >= off[1]/2] + [p >= off[2]/2] at index
+      // p - off[a]/2 of that axis; its cos is table float
+      // tab_off[a] + pos_a npair[a] + p - off[a]/2 and its sin npos_a npair[a]
+      // floats further. Per lane and axis that is a byte offset oc[a] (os[a])
+      // plus 4 i; the loads add it to the table base in scalar registers.
+      // oc[a] >= 0: with even groups off[a]/2 = sum of npair over the axes
+      // before a, and tab_off[a] = sum of 2 npos npair over them, npos >= 1.
       float cv[16], sv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -419,16 +446,23 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const
         sv[i] = 0.f;
       }
       if (!text) {
+        const int p0 = 16 * part;
+        uint32_t oc[3], os[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          const int npos = a == 0 ? kp.T : a == 1 ? kp.Hh : kp.W;
+          oc[a] = 4u * (uint32_t)max(kp.tab_off[a] + coord[a] * kp.npair[a] - (kp.off[a] >> 1) + p0, 0);
+          os[a] = oc[a] + 4u * (uint32_t)(npos * kp.npair[a]);
+        }
+        const int t1 = (kp.off[1] >> 1) - p0, t2 = (kp.off[2] >> 1) - p0;   // first i in axis 1, axis 2
+        const char* tb = reinterpret_cast<const char*>(tab);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int d = 32 * part + 2 * i;
-          const int a = (d >= kp.off[1]) + (d >= kp.off[2]);
-          const int pi = (d - kp.off[a]) >> 1;
-          const int pos = a == 0 ? coord[0] : a == 1 ? coord[1] : coord[2];
-          const int npos = a == 0 ? kp.T : a == 1 ? kp.Hh : kp.W;
-          const float* ct = tab + kp.tab_off[a] + pos * kp.npair[a] + pi;
-          cv[i] = ct[0];
-          sv[i] = ct[npos * kp.npair[a]];
+          const bool ge1 = i >= t1, ge2 = i >= t2;
+          const uint32_t co = (ge2 ? oc[2] : ge1 ? oc[1] : oc[0]) + 4u * i;
+          const uint32_t so = (ge2 ? os[2] : ge1 ? os[1] : os[0]) + 4u * i;
+          cv[i] = *reinterpret_cast<const float*>(tb + co);
+          sv[i] = *reinterpret_cast<const float*>(tb + so);
         }
       }
       if (!text || ROT == 2) {
