@@ -170,6 +170,45 @@ __device__ __forceinline__ int quot_small(int n, int d) {
   return t;
 }
 
+// Sum over the valid tokens of a 64-token block, per dim, of the chunks that
+// the threads of the register kernel hold (thread 64 w + l: token
+// 16 w + l / PARTS, chunk l % PARTS, zero past L): within a wave the lanes
+// PARTS apart are summed by DPP row rotations (by PARTS up to 8 within each row
+// of 16) and the permlane swaps of rows 16 and 32 apart; the four wave sums meet
+// in LDS. Written to dst[0, D) by the first D threads. Called by the whole
+// workgroup.
+template <int D>
+__device__ __forceinline__ void block_sum_chunks(const float (&v)[32], float* dst, float* bs) {
+  constexpr int PARTS = D / 32;
+  float sm[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) sm[e] = v[e];
+  auto row_ror_add = [&](auto ctl_tag) __attribute__((always_inline)) {
+    constexpr int kCtl = decltype(ctl_tag)::value;   // DPP row_ror:n = 0x120 + n
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      sm[e] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sm[e]), kCtl, 0xF, 0xF, false));
+  };
+  if constexpr (PARTS == 2) row_ror_add(std::integral_constant<int, 0x122>());
+  row_ror_add(std::integral_constant<int, 0x124>());
+  row_ror_add(std::integral_constant<int, 0x128>());
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sm[e]), __float_as_uint(sm[e]), false, false);
+    sm[e] = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);   // this lane's value and lane ^ 16's
+    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm[e]), __float_as_uint(sm[e]), false, false);
+    sm[e] = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);   // and lane ^ 32's
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane < PARTS) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) bs[wave * D + 32 * lane + e] = sm[e];
+  }
+  __syncthreads();
+  const int d = threadIdx.x;
+  if (d < D) dst[d] = (bs[d] + bs[D + d]) + (bs[2 * D + d] + bs[3 * D + d]);
+}
+
 // v of lane ^ MASK (MASK 1 or 2) within the lane's aligned group of four, by
 // a DPP quad permutation (no LDS round trip). The 32-value chunks of one
 // token sit in consecutive lanes from a multiple of PARTS (4, or 2 and 6 with
@@ -376,15 +415,16 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(KProblem kp, const __h
   rotate_quantize<D, ROT>(kp, o, b, h, blk, tensor, v, red);
 }
 
-// The same without the LDS tile, for the common call (no RoPE'd copies, no
-// block sums) when every RoPE group starts at an even dim and has an even
-// size, so that each pair (2i, 2i + 1) lies inside one 32-value chunk: each
-// thread loads its chunk of one token with 16-byte loads and applies RoPE in
-// registers (the same products and sums, rounded the same way), then the
-// rotation and quantization as above. No LDS beyond the reductions, so the
-// occupancy is set by the registers. ROT 0 (full Hadamard) or 2 (pair
-// rotation folded into RoPE).
-template <int D, int ROT>
+// The same without the LDS tile, when every RoPE group starts at an even dim
+// and has an even size, so that each pair (2i, 2i + 1) lies inside one
+// 32-value chunk: each thread loads its chunk of one token with 16-byte loads
+// and applies RoPE in registers (the same products and sums, rounded the same
+// way), then the rotation and quantization as above. No LDS beyond the
+// reductions, so the occupancy is set by the registers. ROT 0 (full Hadamard)
+// or 2 (pair rotation folded into RoPE). EXTRA: the instance that may also
+// write the RoPE'd copies and the block sums (more registers; the common call
+// asks for neither).
+template <int D, int ROT, bool EXTRA>
 __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const __half* q, const __half* k,
                                                               const float* tab, QKOut o) {
   static_assert(ROT == 0 || ROT == 2, "chunks of the unpadded row");
@@ -392,17 +432,18 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const
   constexpr int PARTS = S::PARTS, TASKS = S::TASKS;
   static_assert(S::ROUNDS == 1, "one chunk per thread");
   __shared__ float red[4];
+  __shared__ float bs[EXTRA ? 4 * D : 1];   // block sums: one partial row per wave
   const int blk = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
   const __half* x = tensor ? k : q;
 
   float v[1][32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[0][e] = 0.f;
   const int task = threadIdx.x;
   if (task < TASKS) {  // wave-uniform
     const int tok = task / PARTS, part = task - tok * PARTS;
     const int tg = blk * kBlock + tok;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) v[0][e] = 0.f;
     if (tg < kp.L) {
       const __half* src = x + (long long)b * kp.sb + (long long)h * kp.sh + (long long)tg * kp.sl + 32 * part;
 #pragma unroll
@@ -474,8 +515,26 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const
           v[0][2 * i + 1] = fadd_rn(fmul_rn(x0, s), fmul_rn(x1, c));
         }
       }
+      // the RoPE'd fp16 copy of the chunk (the FP16 path's input)
+      __half* rcopy = tensor ? o.k_rope : o.q_rope;
+      if (EXTRA && rcopy != nullptr) {
+        __half* dst = rcopy + ((long long)(b * kp.H + h) * kp.L + tg) * D + 32 * part;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint4 u;
+          __half* hv = reinterpret_cast<__half*>(&u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = __float2half_rn(v[0][8 * c + e]);
+          reinterpret_cast<uint4*>(dst)[c] = u;
+        }
+      }
     }
   }
+  // block sum of the RoPE'd rows over the valid tokens, the representative
+  // token of block-sparse attention before its division by the count
+  // (RainFusion2.0, section 3.2)
+  float* bsum = tensor ? o.k_bsum : o.q_bsum;
+  if (EXTRA && bsum != nullptr) block_sum_chunks<D>(v[0], bsum + ((long long)(b * kp.H + h) * kp.NB + blk) * D, bs);
   rotate_quantize<D, ROT>(kp, o, b, h, blk, tensor, v, red);
 }
 
@@ -508,17 +567,17 @@ hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half*
   dim3 grid(kp.NB, kp.H, 2 * kp.B);
   bool even_pairs = true;
   for (int a = 0; a < 3; ++a) even_pairs = even_pairs && kp.off[a] % 2 == 0 && kp.split[a] % 2 == 0;
-  const bool reg_path = even_pairs && kp.rotation != 1 && o.q_rope == nullptr && o.k_rope == nullptr &&
-                        o.q_bsum == nullptr && o.k_bsum == nullptr;
+  const bool reg_path = even_pairs && kp.rotation != 1;
   if (reg_path) {
-    if (kp.D == 128 && kp.rotation == 0)
-      hipLaunchKernelGGL((qk_prologue_reg_kernel<128, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
-    else if (kp.D == 128)
-      hipLaunchKernelGGL((qk_prologue_reg_kernel<128, 2>), grid, dim3(256), 0, s, kp, q, k, tab, o);
-    else if (kp.D == 64 && kp.rotation == 0)
-      hipLaunchKernelGGL((qk_prologue_reg_kernel<64, 0>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+    const bool extra = o.q_rope != nullptr || o.k_rope != nullptr || o.q_bsum != nullptr || o.k_bsum != nullptr;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, kp, q, k, tab, o); };
+    const bool r0 = kp.rotation == 0;
+    if (kp.D == 128)
+      r0 ? (extra ? go(qk_prologue_reg_kernel<128, 0, true>) : go(qk_prologue_reg_kernel<128, 0, false>))
+         : (extra ? go(qk_prologue_reg_kernel<128, 2, true>) : go(qk_prologue_reg_kernel<128, 2, false>));
     else
-      hipLaunchKernelGGL((qk_prologue_reg_kernel<64, 2>), grid, dim3(256), 0, s, kp, q, k, tab, o);
+      r0 ? (extra ? go(qk_prologue_reg_kernel<64, 0, true>) : go(qk_prologue_reg_kernel<64, 0, false>))
+         : (extra ? go(qk_prologue_reg_kernel<64, 2, true>) : go(qk_prologue_reg_kernel<64, 2, false>));
     return hipGetLastError();
   }
   if (kp.D == 128 && kp.rotation == 0)

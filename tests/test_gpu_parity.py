@@ -30,6 +30,10 @@ CASES = {
     "mixed": W.WORKLOADS["mixed"].replace(H=4, grid=(2, 9, 20)),
     "pair": W.WORKLOADS["tiny"].replace(rotation=W.ROT_PAIR),
     "d64_pair_prefix": W.WORKLOADS["smalld"].replace(H=2, grid=(2, 5, 11), prefix=37, rotation=W.ROT_PAIR),
+    # even RoPE groups at D = 64: the register prologue, with its RoPE'd copies
+    "d64_even": W.WORKLOADS["smalld"].replace(H=2, grid=(2, 5, 11), split=(22, 22, 20)),
+    "d64_even_pair": W.WORKLOADS["smalld"].replace(H=2, grid=(2, 5, 11), prefix=37, split=(22, 22, 20),
+                                                   rotation=W.ROT_PAIR),
     "pair_mixed": W.WORKLOADS["mixed"].replace(H=4, grid=(2, 9, 20), rotation=W.ROT_PAIR),
 }
 
