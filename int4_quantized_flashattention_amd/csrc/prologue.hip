@@ -538,6 +538,99 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const
   rotate_quantize<D, ROT>(kp, o, b, h, blk, tensor, v, red);
 }
 
+// The per-group layout (rotation 1: each RoPE group Walsh-Hadamard rotated
+// alone, zero-padded to 64) without the LDS tile, for even RoPE groups and no
+// block sums. Task (token, chunk c of six) holds dims [32 hf, +32) of group
+// g = c / 2 (hf = c % 2), zero past the group's size (the padding), loaded and
+// RoPE'd a pair at a time in registers; two rounds of 256 tasks, then the
+// rotation and quantization as above. COPY: also the RoPE'd fp16 copy.
+template <int D, bool COPY>
+__global__ __launch_bounds__(256) void qk_prologue_reg_group_kernel(KProblem kp, const __half* q, const __half* k,
+                                                                    const float* tab, QKOut o) {
+  using S = ProShape<D, 1>;
+  constexpr int PARTS = S::PARTS, TASKS = S::TASKS, ROUNDS = S::ROUNDS;
+  static_assert(PARTS == 6 && ROUNDS == 2, "six chunks per token, two rounds");
+  __shared__ float red[4];
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
+  const __half* x = tensor ? k : q;
+  __half* rcopy = tensor ? o.k_rope : o.q_rope;
+
+  float v[ROUNDS][32];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[r][e] = 0.f;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int task = threadIdx.x + 256 * r;
+    const int tok = task / PARTS, c = task - tok * PARTS;
+    const int g = c >> 1, hf = c & 1;
+    const int tg = blk * kBlock + tok;
+    if (task < TASKS && tg < kp.L) {   // (task < TASKS is wave-uniform)
+    // dims [32 hf, 32 hf + nv) of the group are real (nv even; <= 0: none)
+    const int nv = kp.split[g] - 32 * hf;
+    const long long row = (long long)b * kp.sb + (long long)h * kp.sh + (long long)tg * kp.sl + kp.off[g] + 32 * hf;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(x + row);   // even element offset: 4-byte aligned
+    uint32_t raw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) raw[i] = (2 * i < nv) ? src[i] : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const __half2 hv = *reinterpret_cast<const __half2*>(&raw[i]);
+      v[r][2 * i] = __low2float(hv);
+      v[r][2 * i + 1] = __high2float(hv);
+    }
+    if (tg >= kp.prefix) {   // video token: RoPE of the group's pairs 16 hf + i
+      const int idx = tg - kp.prefix, hw = kp.Hh * kp.W;
+      int t, hq;
+      if (kp.L <= (1 << 22)) {   // uniform
+        t = quot_small(idx, hw);
+        hq = quot_small(idx - t * hw, kp.W);
+      } else {
+        t = idx / hw;
+        hq = (idx - t * hw) / kp.W;
+      }
+      const int pos = g == 0 ? t : g == 1 ? hq : idx - t * hw - hq * kp.W;
+      const int npos = g == 0 ? kp.T : g == 1 ? kp.Hh : kp.W;
+      // cos of pair 16 hf + i of axis g at byte oc + 4 i of the table, its sin
+      // npos npair[g] floats further
+      const uint32_t oc = 4u * (uint32_t)(kp.tab_off[g] + pos * kp.npair[g] + 16 * hf);
+      const uint32_t os = oc + 4u * (uint32_t)(npos * kp.npair[g]);
+      const char* tb = reinterpret_cast<const char*>(tab);
+      float cv[16], sv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        cv[i] = 1.f;
+        sv[i] = 0.f;
+        if (2 * i < nv) {
+          cv[i] = *reinterpret_cast<const float*>(tb + oc + 4u * i);
+          sv[i] = *reinterpret_cast<const float*>(tb + os + 4u * i);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x0 = v[r][2 * i], x1 = v[r][2 * i + 1];
+        v[r][2 * i] = fsub_rn(fmul_rn(x0, cv[i]), fmul_rn(x1, sv[i]));
+        v[r][2 * i + 1] = fadd_rn(fmul_rn(x0, sv[i]), fmul_rn(x1, cv[i]));
+      }
+    }
+    if (COPY && rcopy != nullptr) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(rcopy + ((long long)(b * kp.H + h) * kp.L + tg) * D + kp.off[g] +
+                                                  32 * hf);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (2 * i < nv) {
+          const uint32_t lo = __half_as_ushort(__float2half_rn(v[r][2 * i]));
+          const uint32_t hi = __half_as_ushort(__float2half_rn(v[r][2 * i + 1]));
+          dst[i] = lo | (hi << 16);
+        }
+    }
+    }
+  }
+  rotate_quantize<D, 1>(kp, o, b, h, blk, tensor, v, red);
+}
+
 // RoPE only, into a dense fp16 copy (the input of the whole-call FP16 path).
 template <int D>
 __global__ __launch_bounds__(256) void rope_copy_kernel(KProblem kp, const __half* x, const float* tab,
@@ -578,6 +671,15 @@ hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half*
     else
       r0 ? (extra ? go(qk_prologue_reg_kernel<64, 0, true>) : go(qk_prologue_reg_kernel<64, 0, false>))
          : (extra ? go(qk_prologue_reg_kernel<64, 2, true>) : go(qk_prologue_reg_kernel<64, 2, false>));
+    return hipGetLastError();
+  }
+  if (even_pairs && kp.rotation == 1 && o.q_bsum == nullptr && o.k_bsum == nullptr) {
+    const bool copy = o.q_rope != nullptr || o.k_rope != nullptr;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, kp, q, k, tab, o); };
+    if (kp.D == 128)
+      copy ? go(qk_prologue_reg_group_kernel<128, true>) : go(qk_prologue_reg_group_kernel<128, false>);
+    else
+      copy ? go(qk_prologue_reg_group_kernel<64, true>) : go(qk_prologue_reg_group_kernel<64, false>);
     return hipGetLastError();
   }
   if (kp.D == 128 && kp.rotation == 0)

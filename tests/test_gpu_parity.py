@@ -34,6 +34,8 @@ CASES = {
     "d64_even": W.WORKLOADS["smalld"].replace(H=2, grid=(2, 5, 11), split=(22, 22, 20)),
     "d64_even_pair": W.WORKLOADS["smalld"].replace(H=2, grid=(2, 5, 11), prefix=37, split=(22, 22, 20),
                                                    rotation=W.ROT_PAIR),
+    "d64_even_group64": W.WORKLOADS["smalld"].replace(H=2, grid=(1, 3, 30), prefix=5, split=(22, 22, 20),
+                                                      rotation=W.ROT_GROUP64),
     "pair_mixed": W.WORKLOADS["mixed"].replace(H=4, grid=(2, 9, 20), rotation=W.ROT_PAIR),
 }
 
