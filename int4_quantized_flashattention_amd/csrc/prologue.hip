@@ -539,12 +539,14 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_kernel(KProblem kp, const
 }
 
 // The per-group layout (rotation 1: each RoPE group Walsh-Hadamard rotated
-// alone, zero-padded to 64) without the LDS tile, for even RoPE groups and no
-// block sums. Task (token, chunk c of six) holds dims [32 hf, +32) of group
+// alone, zero-padded to 64) without the LDS tile, for even RoPE groups when
+// neither RoPE'd copies nor block sums are asked for (the copies, written a
+// pair at a time from here, made the call slower than the LDS tile's 16-byte
+// stores). Task (token, chunk c of six) holds dims [32 hf, +32) of group
 // g = c / 2 (hf = c % 2), zero past the group's size (the padding), loaded and
 // RoPE'd a pair at a time in registers; two rounds of 256 tasks, then the
-// rotation and quantization as above. COPY: also the RoPE'd fp16 copy.
-template <int D, bool COPY>
+// rotation and quantization as above.
+template <int D>
 __global__ __launch_bounds__(256) void qk_prologue_reg_group_kernel(KProblem kp, const __half* q, const __half* k,
                                                                     const float* tab, QKOut o) {
   using S = ProShape<D, 1>;
@@ -554,7 +556,6 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_group_kernel(KProblem kp,
   const int blk = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z >> 1, tensor = blockIdx.z & 1;
   const __half* x = tensor ? k : q;
-  __half* rcopy = tensor ? o.k_rope : o.q_rope;
 
   float v[ROUNDS][32];
 #pragma unroll
@@ -615,17 +616,6 @@ __global__ __launch_bounds__(256) void qk_prologue_reg_group_kernel(KProblem kp,
         v[r][2 * i + 1] = fadd_rn(fmul_rn(x0, sv[i]), fmul_rn(x1, cv[i]));
       }
     }
-    if (COPY && rcopy != nullptr) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(rcopy + ((long long)(b * kp.H + h) * kp.L + tg) * D + kp.off[g] +
-                                                  32 * hf);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (2 * i < nv) {
-          const uint32_t lo = __half_as_ushort(__float2half_rn(v[r][2 * i]));
-          const uint32_t hi = __half_as_ushort(__float2half_rn(v[r][2 * i + 1]));
-          dst[i] = lo | (hi << 16);
-        }
-    }
     }
   }
   rotate_quantize<D, 1>(kp, o, b, h, blk, tensor, v, red);
@@ -673,13 +663,12 @@ hipError_t launch_qk_prologue(const KProblem& kp, const __half* q, const __half*
          : (extra ? go(qk_prologue_reg_kernel<64, 2, true>) : go(qk_prologue_reg_kernel<64, 2, false>));
     return hipGetLastError();
   }
-  if (even_pairs && kp.rotation == 1 && o.q_bsum == nullptr && o.k_bsum == nullptr) {
-    const bool copy = o.q_rope != nullptr || o.k_rope != nullptr;
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, kp, q, k, tab, o); };
+  if (even_pairs && kp.rotation == 1 && o.q_rope == nullptr && o.k_rope == nullptr && o.q_bsum == nullptr &&
+      o.k_bsum == nullptr) {
     if (kp.D == 128)
-      copy ? go(qk_prologue_reg_group_kernel<128, true>) : go(qk_prologue_reg_group_kernel<128, false>);
+      hipLaunchKernelGGL((qk_prologue_reg_group_kernel<128>), grid, dim3(256), 0, s, kp, q, k, tab, o);
     else
-      copy ? go(qk_prologue_reg_group_kernel<64, true>) : go(qk_prologue_reg_group_kernel<64, false>);
+      hipLaunchKernelGGL((qk_prologue_reg_group_kernel<64>), grid, dim3(256), 0, s, kp, q, k, tab, o);
     return hipGetLastError();
   }
   if (kp.D == 128 && kp.rotation == 0)

@@ -193,3 +193,31 @@ def test_vquant_rounding_ties():
     tie = np.abs(y % 1.0 - 0.5) < 1e-12
     assert tie.sum() > L * D // 2
     assert (c[tie] % 2 == 0).all()
+
+
+@pytest.mark.parametrize("name,w", [
+    ("group64_d128", W.WORKLOADS["480p"].replace(H=2, grid=(2, 7, 23))),
+    ("group64_d64_even", W.WORKLOADS["smalld"].replace(H=2, grid=(1, 3, 30), prefix=5, split=(22, 22, 20),
+                                                       rotation=W.ROT_GROUP64)),
+    ("full_d128", W.WORKLOADS["tiny"].replace(grid=(2, 5, 19), prefix=8)),
+])
+def test_prologue_paths_agree(name, w):
+    """The Q/K prologue with and without RoPE'd copies runs different kernels (per-group layout:
+    the register kernel without copies, the LDS tile with them; full rotation: the register kernel
+    without and with its copy-writing instance); both give the same codes, scales and flags, equal
+    to the oracle's."""
+    G.require_gpu()
+    print(f"[gpu] prologue paths {name} L={w.L} D={w.D} rotation={w.rotation}", flush=True)
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    q, k = G.dev(x["q"]), G.dev(x["k"])
+    a = G.R.rotattn_quantize_qk(p, q, k)
+    c = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    torch.cuda.synchronize()
+    for f in ("q_codes", "k_codes", "q_scale", "k_scale", "q_flag", "k_flag"):
+        assert np.array_equal(G.host(getattr(a, f)), G.host(getattr(c, f))), (name, f)
+    for h in range(w.H):
+        o = G.oracle_head(w, x, 0, h)
+        for t in ("q", "k"):
+            assert np.array_equal(G.unpack_qk_codes(G.host(getattr(a, f"{t}_codes"))[0, h]), o[t]["codes"]), (name, h, t)
+            assert np.array_equal(G.host(getattr(a, f"{t}_scale"))[0, h], o[t]["scale"]), (name, h, t)
