@@ -221,3 +221,24 @@ def test_prologue_paths_agree(name, w):
         for t in ("q", "k"):
             assert np.array_equal(G.unpack_qk_codes(G.host(getattr(a, f"{t}_codes"))[0, h]), o[t]["codes"]), (name, h, t)
             assert np.array_equal(G.host(getattr(a, f"{t}_scale"))[0, h], o[t]["scale"]), (name, h, t)
+
+
+@pytest.mark.parametrize("grid,prefix", [((1, 1, 523), 0), ((523, 1, 1), 3), ((7, 1, 97), 0), ((1, 61, 67), 5),
+                                         ((3, 113, 1), 0), ((2, 3, 251), 11)])
+def test_prologue_grid_coordinates(grid, prefix):
+    """Token coordinates on degenerate and prime-sized grids (the prologue divides by H*W and W with a
+    reciprocal estimate and a correction step): codes, scales and RoPE'd copies equal the oracle's."""
+    G.require_gpu()
+    w = W.WORKLOADS["tiny"].replace(H=1, grid=grid, prefix=prefix)
+    print(f"[gpu] prologue grid {grid} prefix {prefix} L={w.L}", flush=True)
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    for copies in (False, True):
+        qk = G.R.rotattn_quantize_qk(p, G.dev(x["q"]), G.dev(x["k"]), rope_copy=copies)
+        torch.cuda.synchronize()
+        for t in ("q", "k"):
+            o = O.qk_prologue(x[t][0, 0], w.prefix, w.grid, w.split, w.base, w.rotation)
+            assert np.array_equal(G.unpack_qk_codes(G.host(getattr(qk, f"{t}_codes"))[0, 0]), o["codes"]), (grid, t)
+            assert np.array_equal(G.host(getattr(qk, f"{t}_scale"))[0, 0], o["scale"]), (grid, t)
+            if copies:   # the RoPE'd fp16 copy, rounded to nearest even
+                assert np.array_equal(G.host(getattr(qk, f"{t}_rope"))[0, 0], o["rope16"][:w.L]), (grid, t)
