@@ -10,16 +10,23 @@
 // RainFusion2.0, section 3.2 (block means as representative tokens).
 //
 // One workgroup of 256 threads handles one 64-token block of one (b, h,
-// tensor). The block is read once with 16-byte loads, rotated in registers
-// and LDS, and written once as nibble-packed codes: HBM traffic is the
-// compulsory 2 bytes in / D'/2 bytes out per token and head dim.
+// tensor). The block is read once (16-byte loads; 4-byte pairs in the
+// per-group register kernel), rotated in registers (and LDS where the layout
+// needs it), and written once as nibble-packed codes: HBM traffic is the
+// compulsory 2 bytes in / D'/2 bytes out per token and head dim. Three
+// kernels: the register kernel (even RoPE groups, full or pair rotation; a
+// second instance also writes the copies and block sums), the per-group
+// register kernel (even groups, no copies or sums), and the LDS-tile kernel
+// for everything else.
 //
 // Floating-point contract (both sides of the parity tests follow it): each
 // RoPE product and sum is rounded separately (no FMA; the library is built
 // with -ffp-contract=off and uses __fmul_rn and friends), the Hadamard
 // butterflies run in stage order h = 1, 2, 4, ..., then one multiply by
 // float(1/sqrt(n)); scale = absmax / 7 and code = rne(x / scale) as with
-// IEEE division (x * float(1/scale), divided exactly near rounding ties).
+// IEEE division (x * float(1/scale), divided exactly near rounding ties). The
+// error-to-signal sums of the block flag use fused multiply-adds in float32
+// (the flag is exact except where that ratio lies next to the threshold).
 #include "common.h"
 
 namespace rotattn {
