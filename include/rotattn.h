@@ -43,13 +43,14 @@
 extern "C" {
 #endif
 
-#define ROTATTN_VERSION 4
+#define ROTATTN_VERSION 5
 
 /* error codes */
 #define ROTATTN_OK            0
 #define ROTATTN_EINVAL       -1  /* null pointer, bad size, split or stride */
 #define ROTATTN_EUNSUPPORTED -2  /* head dim other than 64 or 128; a RoPE group wider than 64 with ROT_GROUP64;
-                                    L > 2^30, H > 65535, 2B > 65535 or B*H*NB >= 2^24 (launch limits) */
+                                    L > 2^30, H > 65535, 2B > 65535 or B*H*NB >= 2^24 (launch limits); RoPE
+                                    tables of 2^31 floats or more (sum over axes of 2 * grid size * pairs) */
 #define ROTATTN_EALIGN       -3  /* a pointer or row stride not 16-byte aligned */
 #define ROTATTN_EWORKSPACE   -4  /* workspace missing or smaller than rotattn_workspace_bytes */
 #define ROTATTN_ELAUNCH      -5  /* a kernel launch failed */
@@ -153,7 +154,12 @@ int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes);
  * q, k: device fp16 with the problem's strides, 16-byte aligned rows.
  * out: codes, scales, flags, head_kflag (all required); q_rope/k_rope
  * optional (required later by rotattn_attention when FP16 fallback can occur).
- * Workspace: ROTATTN_CALL_QUANTIZE_QK bytes (RoPE tables).
+ * Workspace: ROTATTN_CALL_QUANTIZE_QK bytes. After the call it holds the RoPE
+ * tables the prologue used, from byte 0: for each axis t, h, w in turn,
+ * float32 cos[n_pos][npair] followed by sin[n_pos][npair] (n_pos the grid
+ * size of the axis, npair = rope_split / 2 rounded down), each value
+ * cos/sin(pos * base^(-2i / (2 npair)) (+ pi/4 with ROTATTN_ROT_PAIR))
+ * evaluated in double and rounded once to float.
  */
 int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k,
                         const rotattn_qk_buffers* out, void* workspace, size_t workspace_bytes,
@@ -221,6 +227,8 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
  *   acc_pv  int32 [n_units][64][NB][D] sum over the block of (pq + 8) * v_code
  *                                      (= pq . v + 8 * colsum)
  *   m_hist  float [n_units][64][NB]   running max (log2 domain) after each block
+ *   p15     float [n_units][64][Lp]   the float32 value 15 P that each P code is rounded from
+ *                                      (optional: NULL = not written)
  * Rows at or beyond L are not written. head_fallback as in rotattn_attention.
  * block_mask: NULL (dense) or a block-sparse mask as in
  * rotattn_sparse_attention (then head_fallback must be NULL and
@@ -230,7 +238,7 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                        const uint8_t* head_fallback, const uint32_t* block_mask, const int32_t* units,
                        int32_t n_units,
-                       int32_t* acc_qk, int8_t* p_codes, int32_t* acc_pv, float* m_hist,
+                       int32_t* acc_qk, int8_t* p_codes, int32_t* acc_pv, float* m_hist, float* p15,
                        void* workspace, size_t workspace_bytes, rotattn_stream_t stream);
 
 /*

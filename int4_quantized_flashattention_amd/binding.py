@@ -85,7 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.rotattn_forward.argtypes = [P(Problem), P(QKBuffers), vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_fp16_forward.argtypes = [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_debug_dump.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, vp, C.c_int32,
-                                       vp, vp, vp, vp, vp, C.c_size_t, vp]
+                                       vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_block_mask.argtypes = [P(Problem), P(QKBuffers), C.c_int32, vp, vp, C.c_size_t, vp]
     lib.rotattn_sparse_attention.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, vp, C.c_size_t, vp]
     for name in EXPORTS:
@@ -340,8 +340,9 @@ def mask_to_bool(mask_words, NB: int):
 
 
 def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback=None, ws=None, stream=None,
-                       block_mask=None):
-    """Intermediate integers of the INT4 kernel for 64-row query blocks `units` ((b*H+h)*NB + block)."""
+                       block_mask=None, p15: bool = True):
+    """Intermediate integers of the INT4 kernel for 64-row query blocks `units` ((b*H+h)*NB + block), and (p15)
+    the float32 15 P each P code is rounded from."""
     torch = _torch()
     dev = qk.q_codes.device
     s = get_sizes(p)
@@ -351,13 +352,17 @@ def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback
     pq = torch.zeros((n, 64, s.Lp), dtype=torch.int8, device=dev)
     pv = torch.zeros((n, 64, s.NB, p.D), dtype=torch.int32, device=dev)
     m = torch.full((n, 64, s.NB), float("nan"), dtype=torch.float32, device=dev)
+    y = torch.zeros((n, 64, s.Lp), dtype=torch.float32, device=dev) if p15 else None
     ws, nws = _workspace(p, CALL_DEBUG_DUMP, dev, ws)
     qs, vs = qk.struct(), vq.struct()
     _check(load_library().rotattn_debug_dump(C.byref(p), C.byref(qs), C.byref(vs), _ptr(head_fallback),
                                              _ptr(block_mask), _ptr(units), n, _ptr(acc), _ptr(pq), _ptr(pv),
-                                             _ptr(m),
+                                             _ptr(m), _ptr(y),
                                              _ptr(ws), nws, _stream(stream)), "rotattn_debug_dump")
-    return {"acc": acc, "pq": pq, "accpv": pv, "m": m}
+    out = {"acc": acc, "pq": pq, "accpv": pv, "m": m}
+    if y is not None:
+        out["p15"] = y
+    return out
 
 
 # short aliases

@@ -419,6 +419,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
         s1[v] = exp2_hw(t1);
       }
     }
+    if (DUMP && a.d_p15 != nullptr && wrow + col < L) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
+          a.d_p15[((long long)unit_idx * kBlock + 32 * wave + col) * Lp + key] = s == 0 ? s0[v] : s1[v];
+        }
+    }
     float ls0 = s0[0], ls1 = s1[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) { ls0 += s0[v]; ls1 += s1[v]; }

@@ -202,6 +202,7 @@ struct AttnArgs {
   // dump
   const int32_t* units; int n_units;
   int32_t* d_acc; int8_t* d_pq; int32_t* d_pv; float* d_m;
+  float* d_p15;                 // optional: the float32 15 P each P code is rounded from
 };
 
 hipError_t launch_rope_tables(const KProblem& kp, float* tab, uint32_t* zero_u32, int n_zero, double phase,

@@ -6,6 +6,8 @@
 #include "common.h"
 
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <cmath>
 #include <cstring>
 
@@ -61,17 +63,21 @@ int derive(const rotattn_problem* p, Derived* d) {
   k.NB = (p->L + kBlock - 1) / kBlock;
   k.Lp = k.NB * kBlock;
   k.T = p->grid_t; k.Hh = p->grid_h; k.W = p->grid_w; k.prefix = p->text_prefix;
-  int off = 0, toff = 0;
+  // RoPE tables: cos and sin of every (axis, position, pair), counted in
+  // 64 bits; the kernels index them with 32-bit offsets
+  int off = 0;
+  int64_t toff = 0;
   const int npos[3] = {p->grid_t, p->grid_h, p->grid_w};
   for (int a = 0; a < 3; ++a) {
     k.split[a] = p->rope_split[a];
     k.off[a] = off;
     off += p->rope_split[a];
     k.npair[a] = p->rope_split[a] / 2;
-    k.tab_off[a] = toff;
-    toff += 2 * npos[a] * k.npair[a];
+    k.tab_off[a] = (int)toff;
+    toff += 2 * (int64_t)npos[a] * k.npair[a];
+    if (toff > (int64_t)INT32_MAX) return ROTATTN_EUNSUPPORTED;
   }
-  k.tab_floats = toff;
+  k.tab_floats = (int)toff;
   k.rotation = p->rotation;
   // the mergeable rotation: every RoPE pair turned by pi/4 (folded into RoPE)
   k.pair_phase = (p->rotation == ROTATTN_ROT_PAIR) ? 3.14159265358979323846 / 4.0 : 0.0;
@@ -226,7 +232,7 @@ const char* rotattn_strerror(int code) {
     case ROTATTN_EINVAL: return "invalid argument (null pointer, size, split, grid or stride)";
     case ROTATTN_EUNSUPPORTED:
       return "unsupported problem (head dim must be 64 or 128; RoPE groups <= 64 for ROT_GROUP64; L <= 2^30, "
-             "H <= 65535, 2B <= 65535, B*H*ceil(L/64) < 2^24)";
+             "H <= 65535, 2B <= 65535, B*H*ceil(L/64) < 2^24, RoPE tables < 2^31 floats)";
     case ROTATTN_EALIGN: return "pointer or row stride not 16-byte aligned (workspace: 256-byte)";
     case ROTATTN_EWORKSPACE: return "workspace missing or too small";
     case ROTATTN_ELAUNCH: return "kernel launch failed";
@@ -383,8 +389,8 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                        const uint8_t* head_fallback, const uint32_t* block_mask, const int32_t* units,
                        int32_t n_units, int32_t* acc_qk,
-                       int8_t* p_codes, int32_t* acc_pv, float* m_hist, void* workspace, size_t workspace_bytes,
-                       rotattn_stream_t stream) {
+                       int8_t* p_codes, int32_t* acc_pv, float* m_hist, float* p15, void* workspace,
+                       size_t workspace_bytes, rotattn_stream_t stream) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
@@ -408,7 +414,7 @@ int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, c
   a.v_codes = vq->v_codes; a.v_scale = vq->v_scale;
   a.route = routes(p);
   a.units = units; a.n_units = n_units;
-  a.d_acc = acc_qk; a.d_pq = p_codes; a.d_pv = acc_pv; a.d_m = m_hist;
+  a.d_acc = acc_qk; a.d_pq = p_codes; a.d_pv = acc_pv; a.d_m = m_hist; a.d_p15 = p15;
   a.block_mask = block_mask;
   a.mask_words = (int)((d.NB + 31) / 32);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -37,7 +37,7 @@ def test_exports_match_header():
 
 def test_version_and_strerror():
     lib = _lib()
-    assert lib.rotattn_version() == 4
+    assert lib.rotattn_version() == 5
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.rotattn_strerror(code)
 
@@ -94,6 +94,9 @@ def test_sizes_720p():
     (dict(H=70000), -2),                   # grid y limit
     (dict(B=40000), -2),                   # grid z limit (two tensors per batch)
     (dict(B=1000, H=5000), -2),            # B*H*NB = 2e7 workgroups of 256 on one grid axis
+    # RoPE tables of 2 * 2^25 positions * 64 pairs = 2^32 floats: more than 32-bit offsets address
+    (dict(L=2 ** 25, grid_t=2 ** 25, grid_h=1, grid_w=1, rope_split=(128, 0, 0)), -2),
+    (dict(L=2 ** 23, grid_t=2 ** 23, grid_h=1, grid_w=1, rope_split=(128, 0, 0)), 0),   # 2^30 floats: fine
 ])
 def test_problem_validation(kw, code):
     _lib()
@@ -135,14 +138,14 @@ def test_call_validation_before_launch():
                                     C.c_void_p(good), None, 0, stream) == -4
     # dump with a negative unit count
     assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, None, -1, None, None, None,
-                                  None, None, 0, stream) == -1
+                                  None, None, None, 0, stream) == -1
     # dump without its workspace (the K/V block images)
     one = C.c_void_p(good)
     assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), None, None, one, 1, one, one, one, one,
-                                  None, 0, stream) == -4
+                                  None, None, 0, stream) == -4
     # dump with a block mask and a head mask together
     assert lib.rotattn_debug_dump(C.byref(p), C.byref(qk), C.byref(vb), one, one, one, 1, one, one, one, one,
-                                  None, 0, stream) == -1
+                                  None, None, 0, stream) == -1
     # block mask: needs the block sums; topn < 1; null or misaligned mask (no workspace needed)
     assert Bd.workspace_bytes(p, Bd.CALL_BLOCK_MASK) == 0
     qks = Bd.QKBuffers(*([good] * 7 + [None, None, good, good]))

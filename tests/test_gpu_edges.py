@@ -40,10 +40,7 @@ def _run_and_check(w, x, layout="bhld", tau=None, head_mask=None):
                               q_flags=G.host(qk.q_flag)[b, h].astype(bool),
                               k_flags=G.host(qk.k_flag)[b, h].astype(bool))
             assert np.array_equal(qc[b, h], o["q"]["codes"]), (b, h)
-            tol = G.ATOL + G.RTOL * np.abs(o["out"])
-            if masked:
-                _, bound = G.fp16_weight_bound(o["q"]["rope16"], o["k"]["rope16"], x["v"][b, h], L, D, np.arange(L))
-                tol = tol + bound
+            tol = G.head_output_tol(w, x, b, h, o, masked)
             err = np.abs(got[b, h] - o["out"])
             assert (err <= tol).all(), (b, h, float(err.max()))
     return got
@@ -242,3 +239,29 @@ def test_prologue_grid_coordinates(grid, prefix):
             assert np.array_equal(G.host(getattr(qk, f"{t}_scale"))[0, 0], o["scale"]), (grid, t)
             if copies:   # the RoPE'd fp16 copy, rounded to nearest even
                 assert np.array_equal(G.host(getattr(qk, f"{t}_rope"))[0, 0], o["rope16"][:w.L]), (grid, t)
+
+
+@pytest.mark.parametrize("name,w", [
+    ("720p", W.WORKLOADS["720p"].replace(H=1)),
+    ("smalld_odd_groups", W.WORKLOADS["smalld"].replace(H=1)),
+    ("pair", W.WORKLOADS["tiny"].replace(rotation=W.ROT_PAIR)),
+    ("480p_group64", W.WORKLOADS["480p"].replace(H=1)),
+])
+def test_rope_tables_bitwise(name, w):
+    """The RoPE tables the prologue computed on the device (left in its workspace) equal the oracle's bit for bit:
+    cos/sin of pos * base^(-2i / g_rot) (+ pi/4 for the mergeable rotation) in double, rounded once to float."""
+    G.require_gpu()
+    print(f"[gpu] rope tables {name} grid={w.grid} split={w.split}", flush=True)
+    x = W.full_inputs(w)
+    p = G.R.problem_from_workload(w)
+    n = G.R.workspace_bytes(p, G.R.binding.CALL_QUANTIZE_QK)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    G.R.rotattn_quantize_qk(p, G.dev(x["q"]), G.dev(x["k"]), ws=ws)
+    tab = G.host(ws).view(np.float32)
+    phase = O.pair_phase() if w.rotation == W.ROT_PAIR else 0.0
+    off = 0
+    for a, (c, s) in enumerate(O.rope_tables(w.grid, w.split, w.base, phase)):
+        cnt = c.size
+        assert np.array_equal(tab[off:off + cnt].view(np.uint32), c.ravel().view(np.uint32)), (name, a, "cos")
+        assert np.array_equal(tab[off + cnt:off + 2 * cnt].view(np.uint32), s.ravel().view(np.uint32)), (name, a, "sin")
+        off += 2 * cnt

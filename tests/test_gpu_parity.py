@@ -2,12 +2,15 @@
 
 Bars (bit-exact for integers, the stated tolerance for floating point):
   Q/K/V codes, scales, column sums, int32 Q.K^T and P.V accumulators: bitwise;
-  block flags: exact except where the block's NSR is within 1e-4 of tau;
-  P codes: identical except +-1 where 15 P is within 1e-5 of a rounding
-  boundary, on at most 1e-4 of the entries; P.V accumulators compared on the
-  rows whose P codes all match; running max: bitwise;
-  outputs: |gpu - oracle| <= 2e-3 + 2^-10 |oracle| (quantized path), plus the
-  fp16 weight-rounding bound for tiles on the FP16 path.
+  block flags: exact except where the block's NSR is within 1e-6 tau of tau;
+  P codes: those of the plain quantizer rne(fl(15 P)) - 8, except +-1 where
+  the rounding boundary lies within the derived bound of the oracle's 15 P
+  (gpu_common.p15_plain_and_bound), on at most 1e-4 of the entries; P.V
+  accumulators compared on the rows whose P codes all match; running max:
+  bitwise;
+  outputs: |gpu - oracle| <= 2e-3 + 2^-11 |oracle| plus the derived float32
+  terms of gpu_common.int4_output_tol (INT4 rows, with one code step per
+  boundary flip) and gpu_common.fp16_weight_bound (tiles on the FP16 path).
 """
 import numpy as np
 import pytest
@@ -95,7 +98,7 @@ def test_prologue_parity(name):
         for t in ("q", "k"):
             assert np.array_equal(r[f"{t}_codes"][b, h], o[t]["codes"]), (t, b, h)
             assert np.array_equal(r[f"{t}_scale"][b, h], o[t]["scale"]), (t, b, h)
-            assert G.flags_agree(r[f"{t}_flag"][b, h], o[t]["nsr"], w.tau), (t, b, h)
+            assert G.flags_agree(r[f"{t}_flag"][b, h], o[t]["nsr"], w.tau, w.Dp), (t, b, h)
             assert np.array_equal(r[f"{t}_rope"][b, h], o[t]["rope16"]), (t, b, h)
         assert bool(r["head_kflag"][b * w.H + h]) == bool(r["k_flag"][b, h].any())
 
@@ -109,13 +112,13 @@ def test_vquant_parity(name):
         assert np.array_equal(r["v_colsum"][b, h], o["v_colsum"]), (b, h)
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_int4_loop_parity(name):
-    """Dump of the INT4 kernel (every query block) against the oracle's loop on the same codes and routing."""
-    r = _run(name)
+def _int4_blocks(r):
+    """Oracle loop (with its dump) and the P-code check of every INT4 query block of a case (cached)."""
+    if "int4" in r:
+        return r["int4"]
     w, NB, L = r["w"], r["NB"], r["w"].L
     d = r["dump"]
-    total = mism = 0
+    out = {}
     for (b, h), o in r["oracle"].items():
         masked = r["mask"] is not None and r["mask"][b * w.H + h]
         qf, kf = o["q_flags"], o["k_flags"]
@@ -129,72 +132,70 @@ def test_int4_loop_parity(name):
                                     key_blocks=~kf, dump=True)
             n = rows.size
             keep = np.repeat(~kf, 64)[:L]
-            assert np.array_equal(d["acc"][u, :n, :L][:, keep], ref["acc"][:, :L][:, keep]), (b, h, qb)
-            mh = d["m"][u, :n]
-            dm = np.argwhere(mh[:, ~kf] != ref["m_hist"][:, ~kf])
-            assert dm.size == 0, (b, h, qb, dm[:6].tolist(),
-                                  [(float(mh[:, ~kf][i, j]), float(ref["m_hist"][:, ~kf][i, j])) for i, j in dm[:6]])
-            # oracle P for the tie check
-            gp = d["pq"][u, :n, :L][:, keep]
-            op = ref["pq"][:, :L][:, keep]
-            acc = ref["acc"][:, :L][:, keep].astype(np.float32).astype(np.float64)
-            cq = np.float32(o["q"]["scale"][qb] * O.softmax_c0(w.D))
             kidx = np.nonzero(keep)[0]
-            c = (cq * o["k"]["scale"][kidx // 64]).astype(np.float32).astype(np.float64)
-            m15 = (ref["m_hist"][:, kidx // 64] - O.LOG2_15).astype(np.float32).astype(np.float64)
-            P = np.exp2((acc * c[None, :] - m15).astype(np.float32).astype(np.float64)) * (kidx < L)
-            ok, nb = G.tie_mismatch_ok(gp, op, P)
-            assert ok, (b, h, qb, nb)
-            total += gp.size
-            mism += nb
-            same_rows = np.all(gp == op, axis=1)
-            pv = d["accpv"][u, :n][same_rows][:, ~kf]
-            assert np.array_equal(pv, ref["accpv"][same_rows][:, ~kf]), (b, h, qb)
+            cq = np.float32(o["q"]["scale"][qb] * O.softmax_c0(w.D))
+            c = (cq * o["k"]["scale"][kidx // 64]).astype(np.float32)
+            chk = G.check_p_codes(d["pq"][u, :n, :L][:, keep], d["p15"][u, :n, :L][:, keep],
+                                  ref["acc"][:, :L][:, keep], c, ref["m_hist"][:, kidx // 64])
+            flips = np.zeros((n, L), bool)
+            flips[:, keep] = chk["flips"]
+            out[(b, h, qb)] = {"u": u, "rows": rows, "ref": ref, "chk": chk, "flips": flips, "keep": keep}
+    r["int4"] = out
+    return out
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_int4_loop_parity(name):
+    """Dump of the INT4 kernel (every query block) against the oracle's loop on the same codes and routing.
+
+    Integers (q.k, P.V accumulators) and the running max bitwise; P codes
+    equal to the plain quantizer's except at rounding boundaries within the
+    derived bound, on at most 1e-4 of the entries; the kernel's float32 15 P
+    within the derived bound of the oracle's everywhere.
+    """
+    r = _run(name)
+    d = r["dump"]
+    L = r["w"].L
+    total = mism = 0
+    exp_err = 0.0
+    for (b, h, qb), e in _int4_blocks(r).items():
+        kf = r["oracle"][(b, h)]["k_flags"]
+        u, ref, keep, n = e["u"], e["ref"], e["keep"], e["rows"].size
+        assert np.array_equal(d["acc"][u, :n, :L][:, keep], ref["acc"][:, :L][:, keep]), (b, h, qb)
+        mh = d["m"][u, :n]
+        dm = np.argwhere(mh[:, ~kf] != ref["m_hist"][:, ~kf])
+        assert dm.size == 0, (b, h, qb, dm[:6].tolist())
+        total += e["chk"]["entries"]
+        mism += e["chk"]["mismatch"]
+        exp_err = max(exp_err, e["chk"]["exp_err"])
+        same_rows = ~e["flips"].any(axis=1)
+        pv = d["accpv"][u, :n][same_rows][:, ~kf]
+        assert np.array_equal(pv, ref["accpv"][same_rows][:, ~kf]), (b, h, qb)
+    print(f"[gpu] {name}: P codes {mism} of {total} differ at boundaries; device 2^x max rel err {exp_err:.3g}")
     assert mism <= 1e-4 * max(total, 1), (mism, total)
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_forward_parity(name):
-    """Final fp16 output of rotattn_forward against the oracle (rows with a P-code tie flip are set aside)."""
+    """Final fp16 output of rotattn_forward against the oracle, to the derived per-element tolerance.
+
+    The tolerance (gpu_common.head_output_tol) comes from the oracle alone:
+    every key whose 15 P lies within the derived bound of a rounding
+    boundary may move its code by one step. The P-code check of
+    test_int4_loop_parity confirms the kernel's flips are among those keys.
+    """
     r = _run(name)
-    w, NB, L = r["w"], r["NB"], r["w"].L
-    d = r["dump"]
-    flipped = 0
+    w = r["w"]
+    blocks = _int4_blocks(r)
     for (b, h), o in r["oracle"].items():
-        ref = o["out"]
-        got = r["out"][b, h]
-        tol = G.ATOL + G.RTOL * np.abs(ref)
-        # rows with any FP16 tile: add the fp16 weight-rounding bound
-        masked = r["mask"] is not None and r["mask"][b * w.H + h]
-        qf, kf = o["q_flags"], o["k_flags"]
-        rows_all = np.arange(L)
-        fp16_rows = masked | qf[rows_all // 64]
-        if fp16_rows.any():
-            rr = rows_all[fp16_rows]
-            _, bound = G.fp16_weight_bound(o["q"]["rope16"], o["k"]["rope16"], r["x"]["v"][b, h], L, w.D, rr)
-            tol[rr] += bound
-        if kf.any():
-            rr = rows_all[~fp16_rows]
-            p2, bound = G.fp16_weight_bound(o["q"]["rope16"], o["k"]["rope16"], r["x"]["v"][b, h], L, w.D, rr,
-                                            key_blocks=kf)
-            tol[rr] += bound
-        # rows whose P codes differ from the oracle's at a tie
-        flip = np.zeros(L, bool)
-        for qb in range(NB):
-            if masked or qf[qb]:
-                continue
-            u = (b * w.H + h) * NB + qb
-            rows = np.arange(qb * 64, min(qb * 64 + 64, L))
-            ref_pq = O.int4_flash_rows(o["q"]["codes"], o["q"]["scale"], o["k"]["codes"], o["k"]["scale"],
-                                       o["v_codes"], o["v_scale"], o["v_colsum"], L, w.D, rows,
-                                       key_blocks=~kf, dump=True)["pq"]
-            keep = np.repeat(~kf, 64)[:L]
-            flip[rows] = np.any(d["pq"][u, :rows.size, :L][:, keep] != ref_pq[:, :L][:, keep], axis=1)
-        flipped += int(flip.sum())
-        ok = np.abs(got - ref) <= tol
-        bad = ~ok & ~flip[:, None]
-        assert not bad.any(), (b, h, float(np.abs(got - ref)[~flip].max()), np.argwhere(bad)[:5].tolist())
-    assert flipped <= max(1, 0.01 * w.B * w.H * L)
+        masked = r["mask"] is not None and bool(r["mask"][b * w.H + h])
+        tol = G.head_output_tol(w, r["x"], b, h, o, masked)
+        err = np.abs(r["out"][b, h] - o["out"])
+        bad = err > tol
+        assert not bad.any(), (b, h, float(err.max()), np.argwhere(bad)[:5].tolist(),
+                               [(float(err[i, j]), float(tol[i, j])) for i, j in np.argwhere(bad)[:5]])
+    flipped = sum(int(e["flips"].any(axis=1).sum()) for e in blocks.values())
+    print(f"[gpu] {name}: {flipped} rows carry a P-code boundary flip")
 
 
 @pytest.mark.parametrize("name", ["tiny", "d64_prefix", "ragged_prefix"])
