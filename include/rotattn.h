@@ -14,9 +14,10 @@
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are device (HBM) addresses that the caller
- *    allocates and owns. The library never allocates or frees memory and
- *    keeps no mutable global state; all scratch lives in the caller's
- *    workspace (size from rotattn_workspace_bytes).
+ *    allocates and owns. The library never allocates or frees memory; all
+ *    scratch lives in the caller's workspace (size from
+ *    rotattn_workspace_bytes), except for rotattn_quantize_qk_static, which
+ *    uses a static device buffer of the library (see there).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream). No call synchronizes with the host.
  *  - Return ROTATTN_OK (0) on success or a negative ROTATTN_E* code.
@@ -54,6 +55,7 @@ extern "C" {
 #define ROTATTN_EALIGN       -3  /* a pointer or row stride not 16-byte aligned */
 #define ROTATTN_EWORKSPACE   -4  /* workspace missing or smaller than rotattn_workspace_bytes */
 #define ROTATTN_ELAUNCH      -5  /* a kernel launch failed */
+#define ROTATTN_ESCRATCH     -6  /* more scratch needed than rotattn_quantize_qk_static's static buffer holds */
 
 /* rotation applied after RoPE (RotateAttention abstract, "RoPE-aware Rotation") */
 #define ROTATTN_ROT_FULL    0  /* x' = x H_D / sqrt(D) over the whole head dim; D' = D */
@@ -164,6 +166,22 @@ int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes);
 int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k,
                         const rotattn_qk_buffers* out, void* workspace, size_t workspace_bytes,
                         rotattn_stream_t stream);
+
+/*
+ * rotattn_quantize_qk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, outputs and errors as
+ * rotattn_quantize_qk; its scratch (the RoPE tables) lives in a static
+ * 1 MiB device array of the library, one copy per device, held until the
+ * process ends. Problems whose tables need more than 1 MiB (see
+ * rotattn_workspace_bytes(ROTATTN_CALL_QUANTIZE_QK)) return ROTATTN_ESCRATCH
+ * before anything is enqueued. The stream must belong to the device current
+ * on the calling thread (else ROTATTN_EINVAL). Calls share their device's
+ * array: calls that overlap on one device (different streams, or threads
+ * without ordering between them) race on it. It calls no allocating routine.
+ */
+int rotattn_quantize_qk_static(const rotattn_problem* p, const void* q, const void* k,
+                               const rotattn_qk_buffers* out, rotattn_stream_t stream);
 
 /*
  * Per-channel symmetric INT4 quantization of V over all L tokens of a head,

@@ -28,11 +28,12 @@ CALL_BLOCK_MASK = 6
 CALL_SPARSE_ATTENTION = 7
 
 ERRORS = {0: "ROTATTN_OK", -1: "ROTATTN_EINVAL", -2: "ROTATTN_EUNSUPPORTED", -3: "ROTATTN_EALIGN",
-          -4: "ROTATTN_EWORKSPACE", -5: "ROTATTN_ELAUNCH"}
+          -4: "ROTATTN_EWORKSPACE", -5: "ROTATTN_ELAUNCH", -6: "ROTATTN_ESCRATCH"}
 
 EXPORTS = ["rotattn_version", "rotattn_strerror", "rotattn_get_sizes", "rotattn_workspace_bytes",
            "rotattn_quantize_qk", "rotattn_quantize_v", "rotattn_attention", "rotattn_forward",
-           "rotattn_fp16_forward", "rotattn_debug_dump", "rotattn_block_mask", "rotattn_sparse_attention"]
+           "rotattn_fp16_forward", "rotattn_debug_dump", "rotattn_block_mask", "rotattn_sparse_attention",
+           "rotattn_quantize_qk_static"]
 
 
 class Problem(C.Structure):
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH):
     lib.rotattn_get_sizes.argtypes = [P(Problem), P(Sizes)]
     lib.rotattn_workspace_bytes.argtypes = [P(Problem), C.c_int, P(C.c_size_t)]
     lib.rotattn_quantize_qk.argtypes = [P(Problem), vp, vp, P(QKBuffers), vp, C.c_size_t, vp]
+    lib.rotattn_quantize_qk_static.argtypes = [P(Problem), vp, vp, P(QKBuffers), vp]
     lib.rotattn_quantize_v.argtypes = [P(Problem), vp, P(VBuffers), vp, C.c_size_t, vp]
     lib.rotattn_attention.argtypes = [P(Problem), P(QKBuffers), P(VBuffers), vp, vp, vp, vp, C.c_size_t, vp]
     lib.rotattn_forward.argtypes = [P(Problem), P(QKBuffers), vp, vp, vp, vp, C.c_size_t, vp]
@@ -258,6 +260,18 @@ def rotattn_quantize_qk(p: Problem, q, k, out: QKCodes = None, rope_copy: bool =
     return out
 
 
+def rotattn_quantize_qk_static(p: Problem, q, k, out: QKCodes = None, rope_copy: bool = False, stream=None,
+                               block_sums: bool = False):
+    """rotattn_quantize_qk with the library's static scratch instead of a workspace (no device allocation inside
+    the call; `out` must be given for that: allocating it here is only a convenience)."""
+    if out is None:
+        out = alloc_qk(p, q.device, rope_copy, block_sums)
+    st = out.struct()
+    _check(load_library().rotattn_quantize_qk_static(C.byref(p), _ptr(q), _ptr(k), C.byref(st), _stream(stream)),
+           "rotattn_quantize_qk_static")
+    return out
+
+
 def rotattn_quantize_v(p: Problem, v, out: VCodes = None, ws=None, stream=None):
     if out is None:
         out = alloc_v(p, v.device)
@@ -367,6 +381,7 @@ def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback
 
 # short aliases
 quantize_qk = rotattn_quantize_qk
+quantize_qk_static = rotattn_quantize_qk_static
 quantize_v = rotattn_quantize_v
 attention = rotattn_attention
 forward = rotattn_forward

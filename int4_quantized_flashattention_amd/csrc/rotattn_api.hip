@@ -10,8 +10,15 @@
 #include <cstdint>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 using namespace rotattn;
+
+// Scratch of the allocation-free entry point (rotattn_quantize_qk_static):
+// one copy per device, held until the process ends. It holds the RoPE tables
+// of one call; every call on a device overwrites it.
+constexpr size_t kScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -220,6 +227,57 @@ int check_attention_args(const rotattn_problem* p, const rotattn_qk_buffers* qk,
   return ROTATTN_OK;
 }
 
+int check_quantize_qk(const void* q, const void* k, const rotattn_qk_buffers* out) {
+  if (q == nullptr || k == nullptr) return ROTATTN_EINVAL;
+  const int rc = check_qk(out);
+  if (rc != ROTATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k)) return ROTATTN_EALIGN;
+  return ROTATTN_OK;
+}
+
+// RoPE tables into `tab` (also clears head_kflag), then the Q/K prologue.
+int quantize_qk_impl(const rotattn_problem* p, const Derived& d, const void* q, const void* k,
+                     const rotattn_qk_buffers* out, float* tab, hipStream_t s) {
+  int rc = launched(launch_rope_tables(d.kp, tab, out->head_kflag, p->B * p->H, d.kp.pair_phase, s));
+  if (rc != ROTATTN_OK) return rc;
+  QKOut o;
+  o.q_codes = out->q_codes; o.k_codes = out->k_codes;
+  o.q_scale = out->q_scale; o.k_scale = out->k_scale;
+  o.q_flag = out->q_flag; o.k_flag = out->k_flag;
+  o.head_kflag = out->head_kflag;
+  o.q_rope = static_cast<__half*>(out->q_rope);
+  o.k_rope = static_cast<__half*>(out->k_rope);
+  o.q_bsum = out->q_bsum;
+  o.k_bsum = out->k_bsum;
+  return launched(launch_qk_prologue(d.kp, static_cast<const __half*>(q), static_cast<const __half*>(k), tab, o, s));
+}
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept: in host code the array's name
+// is only a host-side handle, never a device address. The stream must belong
+// to the current device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_on_stream_device(hipStream_t s, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ROTATTN_ELAUNCH;
+  if (s != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return ROTATTN_EINVAL;
+    if (sdev != dev) return ROTATTN_EINVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return ROTATTN_ELAUNCH;
+    g_scratch_dev[dev] = addr;
+  }
+  *ptr = g_scratch_dev[dev];
+  return ROTATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +294,8 @@ const char* rotattn_strerror(int code) {
     case ROTATTN_EALIGN: return "pointer or row stride not 16-byte aligned (workspace: 256-byte)";
     case ROTATTN_EWORKSPACE: return "workspace missing or too small";
     case ROTATTN_ELAUNCH: return "kernel launch failed";
+    case ROTATTN_ESCRATCH:
+      return "problem needs more scratch than the static buffer of the allocation-free entry point holds (1 MiB)";
     default: return "unknown error code";
   }
 }
@@ -279,26 +339,25 @@ int rotattn_quantize_qk(const rotattn_problem* p, const void* q, const void* k, 
   int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
   if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
-  if (q == nullptr || k == nullptr) return ROTATTN_EINVAL;
-  if ((rc = check_qk(out)) != ROTATTN_OK) return rc;
-  if (!aligned16(q) || !aligned16(k)) return ROTATTN_EALIGN;
+  if ((rc = check_quantize_qk(q, k, out)) != ROTATTN_OK) return rc;
   const Layout L = layout(p, d, ROTATTN_CALL_QUANTIZE_QK);
   if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
-  if (p->L == 0) return ROTATTN_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* tab = at<float>(workspace, L.tab);
-  rc = launched(launch_rope_tables(d.kp, tab, out->head_kflag, p->B * p->H, d.kp.pair_phase, s));
+  return quantize_qk_impl(p, d, q, k, out, at<float>(workspace, L.tab), static_cast<hipStream_t>(stream));
+}
+
+int rotattn_quantize_qk_static(const rotattn_problem* p, const void* q, const void* k,
+                               const rotattn_qk_buffers* out, rotattn_stream_t stream) {
+  Derived d;
+  int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
-  QKOut o;
-  o.q_codes = out->q_codes; o.k_codes = out->k_codes;
-  o.q_scale = out->q_scale; o.k_scale = out->k_scale;
-  o.q_flag = out->q_flag; o.k_flag = out->k_flag;
-  o.head_kflag = out->head_kflag;
-  o.q_rope = static_cast<__half*>(out->q_rope);
-  o.k_rope = static_cast<__half*>(out->k_rope);
-  o.q_bsum = out->q_bsum;
-  o.k_bsum = out->k_bsum;
-  return launched(launch_qk_prologue(d.kp, static_cast<const __half*>(q), static_cast<const __half*>(k), tab, o, s));
+  if (p->L == 0) return ROTATTN_OK;   // nothing to do; zero-size buffers may be null
+  if ((rc = check_quantize_qk(q, k, out)) != ROTATTN_OK) return rc;
+  if (layout(p, d, ROTATTN_CALL_QUANTIZE_QK).total > kScratchBytes) return ROTATTN_ESCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scr = nullptr;
+  if ((rc = scratch_on_stream_device(s, &scr)) != ROTATTN_OK) return rc;
+  // the tables are written whole by every call before the prologue reads them: nothing to clear
+  return quantize_qk_impl(p, d, q, k, out, static_cast<float*>(scr), s);
 }
 
 int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_buffers* out, void* workspace,

@@ -38,7 +38,7 @@ def test_exports_match_header():
 def test_version_and_strerror():
     lib = _lib()
     assert lib.rotattn_version() == 5
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert lib.rotattn_strerror(code)
 
 
@@ -174,3 +174,20 @@ def test_empty_problem_is_a_no_op():
     n = Bd.workspace_bytes(p, Bd.CALL_QUANTIZE_QK)
     assert lib.rotattn_quantize_qk(C.byref(p), C.c_void_p(good), C.c_void_p(good), C.byref(qk), ws, n,
                                    C.c_void_p(None)) == 0
+
+
+def test_static_quantize_qk_validation():
+    """The allocation-free Q/K entry point: argument errors, and problems whose RoPE tables exceed its 1 MiB static
+    scratch, are refused before any device call."""
+    lib = _lib()
+    good = 1 << 20
+    qk = Bd.QKBuffers(*([good] * 7 + [None] * 4))
+    p = _p()
+    assert lib.rotattn_quantize_qk_static(C.byref(p), None, C.c_void_p(good), C.byref(qk), None) == -1
+    assert lib.rotattn_quantize_qk_static(C.byref(p), C.c_void_p(good + 2), C.c_void_p(good), C.byref(qk), None) == -3
+    big = _p(L=2 ** 23, grid_t=2 ** 23, grid_h=1, grid_w=1, rope_split=(128, 0, 0))   # 4 GiB of tables
+    assert Bd.workspace_bytes(big, Bd.CALL_QUANTIZE_QK) > (1 << 20)
+    assert lib.rotattn_quantize_qk_static(C.byref(big), C.c_void_p(good), C.c_void_p(good), C.byref(qk), None) == -6
+    # the 720p tables (21 + 45 + 80 positions) fit easily
+    assert Bd.workspace_bytes(Bd.problem_from_workload(W.WORKLOADS["720p"]), Bd.CALL_QUANTIZE_QK) < (1 << 20)
+
