@@ -209,20 +209,21 @@ def main():
     qk = R.binding.alloc_qk(p, dev, need_rope)
     vq = R.binding.alloc_v(p, dev)
     out = torch.empty((w.B, w.H, w.L, w.D), dtype=torch.float16, device=dev)
+    att_call = R.binding.CALL_ATTENTION if mask is None else R.binding.CALL_ATTENTION_HEAD_FALLBACK
     ws = {c: (torch.empty(max(1, R.workspace_bytes(p, c)), dtype=torch.uint8, device=dev))
-          for c in (R.binding.CALL_QUANTIZE_QK, R.binding.CALL_QUANTIZE_V, R.binding.CALL_ATTENTION)}
+          for c in (R.binding.CALL_QUANTIZE_QK, R.binding.CALL_QUANTIZE_V, att_call)}
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        R.rotattn_quantize_qk(p, q, k, out=qk, ws=ws[0], stream=stream)
+        R.rotattn_quantize_qk(p, q, k, out=qk, ws=ws[R.binding.CALL_QUANTIZE_QK], stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        R.rotattn_quantize_v(p, v, out=vq, ws=ws[1], stream=stream)
+        R.rotattn_quantize_v(p, v, out=vq, ws=ws[R.binding.CALL_QUANTIZE_V], stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        R.rotattn_attention(p, qk, vq, v=v if need_rope else None, head_fallback=mask, out=out, ws=ws[2],
+        R.rotattn_attention(p, qk, vq, v=v if need_rope else None, head_fallback=mask, out=out, ws=ws[att_call],
                             stream=stream)
         if ev is not None:
             ev[3].record(stream)

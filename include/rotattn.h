@@ -73,6 +73,8 @@ extern "C" {
 #define ROTATTN_CALL_DEBUG_DUMP  5
 #define ROTATTN_CALL_BLOCK_MASK  6
 #define ROTATTN_CALL_SPARSE_ATTENTION 7
+#define ROTATTN_CALL_ATTENTION_HEAD_FALLBACK 8  /* rotattn_attention with a head_fallback mask */
+#define ROTATTN_CALL_FORWARD_HEAD_FALLBACK   9  /* rotattn_forward with a head_fallback mask */
 
 typedef void* rotattn_stream_t; /* hipStream_t */
 
@@ -97,7 +99,7 @@ typedef struct rotattn_qk_buffers {
   float* k_scale;
   uint8_t* q_flag;      /* [B][H][NB] 1 if the block's quantization NSR > block_err_tau */
   uint8_t* k_flag;
-  uint32_t* head_kflag; /* [B*H] nonzero if any K block of the head is flagged */
+  uint32_t* head_kflag; /* [B*H] number of flagged K blocks of the head (nonzero if any is flagged) */
   void* q_rope;         /* optional fp16 [B][H][L][D] (dense): RoPE'd, unrotated Q for the FP16 path (with
                            ROTATTN_ROT_PAIR the pair rotation is part of RoPE and included); NULL = not written */
   void* k_rope;         /* optional, as q_rope */
@@ -201,17 +203,23 @@ int rotattn_quantize_v(const rotattn_problem* p, const void* v, const rotattn_v_
  * out = O * (s_v / 15) / l in fp16.
  * Routing (selective FP16 fallback): tile (query block i, key block j) runs
  * on the FP16 path when head_fallback[b*H+h] != 0, or q_flag[i], or
- * k_flag[j]; query blocks that mix both paths merge the two partial results
- * by log-sum-exp.
+ * k_flag[j]. A query block that mixes both paths runs its INT4 tiles first
+ * (their running max, and so their P codes, see the INT4 tiles only); its
+ * FP16 tiles then continue the same online softmax (in a head with at most
+ * 16 flagged K blocks), or run as a partial result of their own merged with
+ * the INT4 one (more than 16): either is the log-sum-exp merge of the two
+ * partial results.
  * head_fallback: device uint8 [B*H] or NULL (no head is masked). When it is
  * non-NULL or block_err_tau is finite, qk->q_rope and qk->k_rope and v are
  * required (the FP16 path reads them); otherwise they may be NULL.
  * out: device fp16 with the problem's strides (may not alias inputs).
- * Workspace: ROTATTN_CALL_ATTENTION bytes: the K/V block images the INT4
- * kernel copies into LDS (1.5x the packed K + V codes at D' = D = 128), the transposed
- * fp16 V blocks of the FP16 path (L x D fp16 rounded up to whole blocks;
- * written only when the FP16 path runs), plus the partial results of mixed
- * rows when block_err_tau is finite.
+ * Workspace: ROTATTN_CALL_ATTENTION bytes without a head mask,
+ * ROTATTN_CALL_ATTENTION_HEAD_FALLBACK bytes with one: the K/V block images
+ * the INT4 kernel copies into LDS (1.5x the packed K + V codes at
+ * D' = D = 128); when the FP16 path can run (a head mask, or
+ * block_err_tau finite), the transposed fp16 V blocks it reads (L x D fp16
+ * rounded up to whole blocks); with block_err_tau finite, room for the INT4
+ * partial results of rows that mix both paths (float32 O, m, l per row).
  */
 int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,
                       const void* v, const uint8_t* head_fallback, void* out,
@@ -219,8 +227,10 @@ int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, co
 
 /*
  * rotattn_quantize_v into the workspace followed by rotattn_attention: the
- * whole attention call after rotattn_quantize_qk.
- * Workspace: ROTATTN_CALL_FORWARD bytes.
+ * whole attention call after rotattn_quantize_qk (steps 3 for V and 4 of the
+ * RotateAttention abstract's path, with its selective FP16 fallback).
+ * Workspace: ROTATTN_CALL_FORWARD bytes without a head mask,
+ * ROTATTN_CALL_FORWARD_HEAD_FALLBACK bytes with one.
  */
 int rotattn_forward(const rotattn_problem* p, const rotattn_qk_buffers* qk, const void* v,
                     const uint8_t* head_fallback, void* out,

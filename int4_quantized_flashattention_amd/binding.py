@@ -26,6 +26,8 @@ CALL_FP16_FORWARD = 4
 CALL_DEBUG_DUMP = 5
 CALL_BLOCK_MASK = 6
 CALL_SPARSE_ATTENTION = 7
+CALL_ATTENTION_HEAD_FALLBACK = 8
+CALL_FORWARD_HEAD_FALLBACK = 9
 
 ERRORS = {0: "ROTATTN_OK", -1: "ROTATTN_EINVAL", -2: "ROTATTN_EUNSUPPORTED", -3: "ROTATTN_EALIGN",
           -4: "ROTATTN_EWORKSPACE", -5: "ROTATTN_ELAUNCH", -6: "ROTATTN_ESCRATCH"}
@@ -288,7 +290,7 @@ def rotattn_attention(p: Problem, qk: QKCodes, vq: VCodes, v=None, head_fallback
     dev = qk.q_codes.device
     if out is None:
         out = torch.empty((p.B, p.H, p.L, p.D), dtype=torch.float16, device=dev)
-    ws, n = _workspace(p, CALL_ATTENTION, dev, ws)
+    ws, n = _workspace(p, CALL_ATTENTION if head_fallback is None else CALL_ATTENTION_HEAD_FALLBACK, dev, ws)
     qs, vs = qk.struct(), vq.struct()
     _check(load_library().rotattn_attention(C.byref(p), C.byref(qs), C.byref(vs), _ptr(v), _ptr(head_fallback),
                                             _ptr(out), _ptr(ws), n, _stream(stream)), "rotattn_attention")
@@ -299,7 +301,7 @@ def rotattn_forward(p: Problem, qk: QKCodes, v, head_fallback=None, out=None, ws
     torch = _torch()
     if out is None:
         out = torch.empty((p.B, p.H, p.L, p.D), dtype=torch.float16, device=v.device)
-    ws, n = _workspace(p, CALL_FORWARD, v.device, ws)
+    ws, n = _workspace(p, CALL_FORWARD if head_fallback is None else CALL_FORWARD_HEAD_FALLBACK, v.device, ws)
     qs = qk.struct()
     _check(load_library().rotattn_forward(C.byref(p), C.byref(qs), _ptr(v), _ptr(head_fallback), _ptr(out),
                                           _ptr(ws), n, _stream(stream)), "rotattn_forward")

@@ -1,7 +1,9 @@
 // FP16 flash-attention path: the selective FP16 fallback of RotateAttention
-// (arXiv 2607.02584, abstract) for masked heads, flagged Q/K blocks and whole
-// denoising steps, with the log-sum-exp merge of mixed query blocks fused
-// into its epilogue.
+// (arXiv 2607.02584, abstract) for masked heads, flagged Q blocks and whole
+// denoising steps, and for the flagged K blocks of rows that mix both paths
+// in heads with many flagged K blocks (more than kInlineMaxFlags), whose INT4
+// partials it merges by log-sum-exp in its epilogue. (In heads with few, the
+// INT4 kernel finishes such rows itself.)
 //
 // Recurrences: RainFusion2.0, section 3.1 "Blockwise Sparse", in the log2
 // domain over key blocks of 64; a tile that belongs to the INT4 path is
@@ -28,8 +30,6 @@ __device__ __forceinline__ float exp2_hw16(float x) { return __builtin_amdgcn_ex
 // XOR-permuted per row), then D rows of V^T, 64 halves each (permuted the same
 // way as 128-byte rows). 256 * D bytes; the pre-pass writes the V^T half.
 template <int D>
-__host__ __device__ constexpr int f16_vt_bytes() { return 128 * D; }
-template <int D>
 __device__ __forceinline__ int f16_kswz(int r) { return D == 128 ? (r & 15) : kv_swz(128, r); }
 // key (within the block) whose value sits at position pos of a V^T row: the
 // order in which the P operand of the second product holds its keys
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void fp16_vt_kernel(KProblem kp, const __half*
   const long long bh = u / kp.NB;
   const int j = (int)(u - bh * kp.NB);
   const int b = (int)(bh / kp.H), h = (int)(bh - (long long)b * kp.H);
-  uint8_t* dst = image + u * f16_vt_bytes<D>();
+  uint8_t* dst = image + u * f16_vt_bytes(D);
   for (int idx = threadIdx.x; idx < kBlock * D / 8; idx += 256) {
     const int r = idx / (D / 8), pc = idx - r * (D / 8);
     const int key = j * kBlock + r;
@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void fp16_vt_kernel(KProblem kp, const __half*
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs a, int whole_call, float c0) {
+__global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs a, int rows_sel, float c0) {
   constexpr int NC = D / 16;       // 16-deep slices of the head dim
   constexpr int NCT = D / 32;      // 32-channel output tiles
-  constexpr int KROWB = 2 * D, VT0 = 64 * KROWB, VTB = f16_vt_bytes<D>();
+  constexpr int KROWB = 2 * D, VT0 = 64 * KROWB, VTB = f16_vt_bytes(D);
   constexpr int IMG = VT0 + VTB;
   constexpr int NDK = VT0 / 4096, NDV = VTB / 4096;   // 16-byte copies per thread per stage
   static_assert(VT0 % 4096 == 0 && VTB % 4096 == 0, "a stage must split evenly over the workgroup");
@@ -87,9 +87,11 @@ __global__ __launch_bounds__(256, 2) void fp16_attn_kernel(KProblem kp, AttnArgs
   // flagged key blocks only (their other blocks ran on the INT4 path)
   bool full = false, mixed = false;
   if (active) {
-    full = whole_call || (a.head_mask != nullptr && uniform_byte(a.head_mask, bh) != 0) ||
+    full = rows_sel == kFp16WholeCall || (a.head_mask != nullptr && uniform_byte(a.head_mask, bh) != 0) ||
            (a.route && uniform_byte(a.q_flag, bh * NB + qblk) != 0);
-    mixed = !full && a.route && a.head_kflag[bh] != 0;
+    mixed = !full && a.route && a.head_kflag[bh] > kInlineMaxFlags;
+    if (rows_sel == kFp16FullOnly) mixed = false;
+    if (rows_sel == kFp16MergeOnly) full = false;
   }
   const bool any_full = __builtin_amdgcn_readfirstlane(__syncthreads_or(full)) != 0;
   const bool any_mixed = __builtin_amdgcn_readfirstlane(__syncthreads_or(mixed)) != 0;
@@ -328,13 +330,13 @@ hipError_t launch_fp16_vt(const KProblem& kp, const __half* v, uint8_t* image, h
   return hipGetLastError();
 }
 
-hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, bool whole_call, hipStream_t s) {
+hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, Fp16Rows rows, hipStream_t s) {
   const float c0 = (float)(std::log2(2.718281828459045) / std::sqrt((double)kp.D));
   dim3 grid((kp.L + 127) / 128, kp.H, kp.B);
   if (kp.D == 128)
-    hipLaunchKernelGGL((fp16_attn_kernel<128>), grid, dim3(256), 0, s, kp, a, whole_call ? 1 : 0, c0);
+    hipLaunchKernelGGL((fp16_attn_kernel<128>), grid, dim3(256), 0, s, kp, a, (int)rows, c0);
   else if (kp.D == 64)
-    hipLaunchKernelGGL((fp16_attn_kernel<64>), grid, dim3(256), 0, s, kp, a, whole_call ? 1 : 0, c0);
+    hipLaunchKernelGGL((fp16_attn_kernel<64>), grid, dim3(256), 0, s, kp, a, (int)rows, c0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

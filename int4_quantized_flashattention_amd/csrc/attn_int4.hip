@@ -120,6 +120,94 @@ __global__ __launch_bounds__(256) void kv_image_kernel(KProblem kp, const uint8_
 // operand format code of FP6 E2M3 in v_mfma_*_f8f6f4 (cbsz / blgp)
 constexpr int kFp6 = 2;
 
+// The FP16 tiles of a row that mixes both paths (RotateAttention abstract,
+// selective FP16 fallback; tile routing: head mask, Q flag or K flag), in a
+// head with few flagged K blocks, run after the row's INT4 loop has
+// finished. The online softmax of RainFusion2.0, section 3.1 continues from
+// the INT4 state (m, l, o in V's units) over the head's flagged key blocks in
+// ascending order: S^T = K Q^T and O^T = V^T P^T with
+// v_mfma_f32_32x32x16_f16 on the RoPE'd, unrotated fp16 Q/K and the V^T block
+// images of the FP16 path, P rounded to fp16 for the product and l summed
+// from the float32 P. Continuing one recurrence from the other's final state
+// is the log-sum-exp merge of the two partial results, and the INT4 codes are
+// unaffected: that loop's running max saw its own tiles only. The operands are
+// read straight from global memory (L2), which suits a few blocks and keeps
+// the INT4 loop's registers and LDS; the lanes of rows past L take part with
+// clamped rows and store nothing.
+template <int DV>
+__device__ __forceinline__ void fp16_tiles_of_mixed_row(const KProblem& kp, const AttnArgs& a, int bh, int row,
+                                                        int col, int hh, float c0, float& m, float& l,
+                                                        v16f (&o)[DV / 32]) {
+  constexpr int NC = DV / 16, NCT = DV / 32, VTB = f16_vt_bytes(DV);
+  const int L = kp.L, NB = kp.NB;
+  const uint64_t kflag_s = uniform_ptr(a.k_flag + (long long)bh * NB);
+  const __half* qrow = a.q_rope + ((long long)bh * L + min(row, L - 1)) * DV + 8 * hh;
+  const __half* kbase = a.k_rope + (long long)bh * L * DV + 8 * hh;
+  const uint8_t* vbase = a.f16_vt + (long long)bh * NB * VTB;
+  for (int j = 0; j < NB; ++j) {
+    if (uniform_byte_u(kflag_s, j) == 0) continue;
+    v16f sacc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[s][v] = 0.f;
+      const __half* krow = kbase + (long long)min(j * kBlock + 32 * s + col, L - 1) * DV;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const v8h kop = *reinterpret_cast<const v8h*>(krow + 16 * c);
+        const v8h qop = *reinterpret_cast<const v8h*>(qrow + 16 * c);
+        sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop, sacc[s], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = j * kBlock + 32 * s + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (key >= L) sacc[s][v] = -INFINITY;
+        mx = smax(mx, sacc[s][v]);
+      }
+    {  // the other 32 keys of this query sit in lane ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // block j holds a key below L, so m_new is finite; alpha = 0 while m = -inf
+    const float m_new = smax(m, mx * c0);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[ct][v] *= alpha;
+    l *= alpha;
+    m = m_new;
+    v8h pop[2][2];
+    float ps = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[s][v], c0, -m));
+        ps += p;
+        pop[s][v >> 3][v & 7] = (_Float16)p;
+      }
+    l += ps + __shfl_xor(ps, 32);
+    const uint8_t* vblk = vbase + (long long)j * VTB;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int ch = ct * 32 + col;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int pc = 2 * (2 * s + u) + hh;   // logical 16-byte piece: the P operand's keys
+          const v8h vop = *reinterpret_cast<const v8h*>(vblk + ch * 128 + 16 * (pc ^ kv_swz(128, ch)));
+          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[s][u], o[ct], 0, 0, 0);
+        }
+    }
+  }
+}
+
 // One workgroup = NW waves = 32*NW query rows of one (b, h). Per key block of
 // 64, the block's LDS image (FP6 K rows and FP6 V^T rows, each split into
 // 16- and 8-byte planes) arrives in one stage of an NST-stage ring through direct-to-LDS loads issued NST - 1
@@ -130,7 +218,13 @@ constexpr int kFp6 = 2;
 // SPARSE: block-sparse attention (RainFusion2.0, section 3.1: Q_i K_j^T and
 // P_ij V_j are skipped where M_ij = 0), with one mask row per 128-row query
 // block: the loop visits only the key blocks that row keeps.
-template <int DP, int DV, int NW, int NST, int OCC, bool DUMP, bool SPARSE>
+// ROUTE: the instance for calls with block routing (tau finite), which can
+// meet rows that mix both paths: in a head with few flagged K blocks such a
+// row finishes its FP16 tiles here after its INT4 loop
+// (fp16_tiles_of_mixed_row); in a head with more it writes its INT4 partial
+// result for the FP16 kernel to merge. The other instances never meet such
+// rows and keep their registers for the loop.
+template <int DP, int DV, int NW, int NST, int OCC, bool DUMP, bool SPARSE, bool ROUTE>
 __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, AttnArgs a, float c0, float log2_15) {
   constexpr int NT = NW * 64;
   constexpr int NC = DP / 64;              // 64-deep slices of the rotated head dim (one FP6 product each)
@@ -549,43 +643,70 @@ __global__ __launch_bounds__(NW * 64, OCC) void int4_attn_kernel(KProblem kp, At
   if (DUMP || !work) return;
   const float l15t = l15 + __shfl_xor(l15, 32);
   const int row = wrow + col;
-  if (row >= L) return;
   const float* svp = a.v_scale + (long long)bh * DV;
-  if (!mixed) {
-    // out = O (s_v / 15) / l with O = 2^3 o and l = l15 / 15 (a sparse row
-    // that keeps no key block gets zeros)
-    const float inv = (SPARSE && l15t == 0.f) ? 0.f : 8.0f / l15t;
-    __half* orow = a.out + (long long)b * kp.sb + (long long)h * kp.sh + (long long)row * kp.sl;
+  __half* orow = a.out + (long long)b * kp.sb + (long long)h * kp.sh + (long long)row * kp.sl;
+  if constexpr (ROUTE && !DUMP && !SPARSE) {
+    if (mixed) {
+      if (a.head_kflag[bh] <= kInlineMaxFlags) {
+        // the INT4 partial in V's units: O = 2^3 o s_v / 15 and l = l15 / 15,
+        // at m_run; then the FP16 tiles
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ch = ct * 32 + 8 * g + 4 * hh;
-        __half hv[4];
+          for (int v = 0; v < 16; ++v) o[ct][v] *= svp[ct * 32 + 8 * (v >> 2) + 4 * hh + (v & 3)] * (8.0f / 15.0f);
+        float l = l15t * (1.0f / 15.0f);
+        fp16_tiles_of_mixed_row<DV>(kp, a, bh, row, col, hh, c0, m_run, l, o);
+        if (row >= L) return;
+        const float inv = 1.0f / l;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn(o[ct][4 * g + e] * svp[ch + e] * inv);
-        *reinterpret_cast<uint2*>(orow + ch) = *reinterpret_cast<const uint2*>(hv);
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int ch = ct * 32 + 8 * g + 4 * hh;
+            __half hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn(o[ct][4 * g + e] * inv);
+            *reinterpret_cast<uint2*>(orow + ch) = *reinterpret_cast<const uint2*>(hv);
+          }
+        return;
       }
-  } else {
-    float* po = a.part_o + ((long long)bh * Lp + row) * DV;
+      // many flagged K blocks: the INT4 partial (O s_v / 15 with O = 2^3 o;
+      // m; l = l15 / 15) for the FP16 kernel to merge
+      if (row >= L) return;
+      float* po = a.part_o + ((long long)bh * Lp + row) * DV;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ch = ct * 32 + 8 * g + 4 * hh;
-        float4 f;
-        // O (s_v / 15) with O = 2^3 o
-        f.x = o[ct][4 * g + 0] * (svp[ch + 0] * (8.0f / 15.0f));
-        f.y = o[ct][4 * g + 1] * (svp[ch + 1] * (8.0f / 15.0f));
-        f.z = o[ct][4 * g + 2] * (svp[ch + 2] * (8.0f / 15.0f));
-        f.w = o[ct][4 * g + 3] * (svp[ch + 3] * (8.0f / 15.0f));
-        *reinterpret_cast<float4*>(po + ch) = f;
+        for (int g = 0; g < 4; ++g) {
+          const int ch = ct * 32 + 8 * g + 4 * hh;
+          float4 f;
+          f.x = o[ct][4 * g + 0] * (svp[ch + 0] * (8.0f / 15.0f));
+          f.y = o[ct][4 * g + 1] * (svp[ch + 1] * (8.0f / 15.0f));
+          f.z = o[ct][4 * g + 2] * (svp[ch + 2] * (8.0f / 15.0f));
+          f.w = o[ct][4 * g + 3] * (svp[ch + 3] * (8.0f / 15.0f));
+          *reinterpret_cast<float4*>(po + ch) = f;
+        }
+      if (hh == 0) {
+        a.part_m[(long long)bh * Lp + row] = m_run;
+        a.part_l[(long long)bh * Lp + row] = l15t * (1.0f / 15.0f);
       }
-    if (hh == 0) {
-      a.part_m[(long long)bh * Lp + row] = m_run;
-      a.part_l[(long long)bh * Lp + row] = l15t * (1.0f / 15.0f);
+      return;
     }
   }
+  if (row >= L) return;
+  // out = O (s_v / 15) / l with O = 2^3 o and l = l15 / 15 (a sparse row
+  // that keeps no key block gets zeros)
+  const float inv = (SPARSE && l15t == 0.f) ? 0.f : 8.0f / l15t;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = ct * 32 + 8 * g + 4 * hh;
+      __half hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[e] = __float2half_rn(o[ct][4 * g + e] * svp[ch + e] * inv);
+      *reinterpret_cast<uint2*>(orow + ch) = *reinterpret_cast<const uint2*>(hv);
+    }
 }
 
 // Launch shape per rotated head dim. Four waves per workgroup (32 query rows
@@ -610,13 +731,20 @@ static void launch_int4_s(const KProblem& kp, const AttnArgs& a, bool dump, floa
   using S = Shape<DP, DV>;
   constexpr int W = S::kWaves, NS = S::kStages, OC = S::kOcc;
   if (dump) {
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true, SPARSE>), dim3(a.n_units), dim3(W * 64), 0, s,
-                       kp, a, c0, l15);
+    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, true, SPARSE, false>), dim3(a.n_units), dim3(W * 64),
+                       0, s, kp, a, c0, l15);
   } else {
     const int ntiles = (kp.L + 32 * W - 1) / (32 * W);
     dim3 grid(ntiles * kp.H * kp.B);
-    hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false, SPARSE>), grid, dim3(W * 64), 0, s, kp, a, c0,
-                       l15);
+    // the routed instance: two workgroups per CU at D' = 128, where three
+    // would make it spill; at D' = 192 held to the registers of three
+    constexpr int OCR = (DP == 128) ? 2 : (DP == 192 && DV == 128) ? 3 : OC;
+    if (!SPARSE && a.route)
+      hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OCR, false, SPARSE, !SPARSE>), grid, dim3(W * 64), 0, s,
+                         kp, a, c0, l15);
+    else
+      hipLaunchKernelGGL((int4_attn_kernel<DP, DV, W, NS, OC, false, SPARSE, false>), grid, dim3(W * 64), 0, s, kp,
+                         a, c0, l15);
   }
 }
 

@@ -75,6 +75,18 @@ __host__ __device__ constexpr int kv_swz(int row_bytes, int r) {
   return row_bytes == 128 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
+// FP16 path: the V^T image of one (b, h, 64-key block) that fp16_vt_kernel
+// writes: D rows (channels) of 64 halves (128 bytes), the keys in the order in
+// which the P operand of the FP16 P.V product holds them, the 16-byte pieces
+// of row ch XOR-permuted by kv_swz(128, ch).
+__host__ __device__ constexpr int f16_vt_bytes(int D) { return 128 * D; }
+
+// A row that mixes both paths finishes its FP16 tiles inside the INT4 kernel
+// when its head has at most this many flagged K blocks; a head with more has
+// its INT4 partial results merged by the FP16 kernel, which stages the K/V
+// blocks through LDS.
+constexpr unsigned kInlineMaxFlags = 16;
+
 // s_waitcnt that waits until at most N vector-memory operations of this wave
 // are outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
 template <int N>
@@ -192,12 +204,12 @@ struct AttnArgs {
   const uint8_t* head_mask;     // [B*H] or null
   const uint8_t* v_codes; const float* v_scale;
   const uint8_t* kv_image;      // [B*H][NB] LDS images of the K/V blocks (kv_image_bytes each)
-  const uint8_t* f16_vt;        // [B*H][NB] V^T blocks of the FP16 path (128 * D bytes each)
+  const uint8_t* f16_vt;        // [B*H][NB] V^T blocks of the FP16 path (f16_vt_bytes(D) each)
   const uint32_t* block_mask;   // block-sparse: [B*H][ceil(NB/2)][mask_words] key-block bits per 128-row query block
   int mask_words;               // ceil(NB / 32)
   const __half* q_rope; const __half* k_rope; const __half* v;   // FP16 path inputs
   __half* out;
-  float* part_o; float* part_m; float* part_l;   // INT4 partials of mixed rows [B][H][Lp][D], [B][H][Lp]
+  float* part_o; float* part_m; float* part_l;   // INT4 partials of split rows [B][H][Lp][D], [B][H][Lp]
   bool route;                   // block routing possible (tau finite)
   // dump
   const int32_t* units; int n_units;
@@ -218,5 +230,12 @@ hipError_t launch_block_topn(const KProblem& kp, const float* q_bsum, const floa
 constexpr int kMaxMaskBlocks = 16384;   // largest NB the block-mask builder takes (L <= 1048576)
 constexpr int kMaskQBlock = 128;        // query rows per block-sparse mask row (one INT4 workgroup)
 hipError_t launch_fp16_vt(const KProblem& kp, const __half* v, uint8_t* image, hipStream_t s);
-hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, bool whole_call, hipStream_t s);
+// which rows the FP16 kernel takes
+enum Fp16Rows : int {
+  kFp16Routed = 0,     // rows that run whole on FP16 and the merges of INT4 partials
+  kFp16WholeCall = 1,  // every row
+  kFp16FullOnly = 2,   // rows that run whole on FP16 (masked heads, flagged Q blocks)
+  kFp16MergeOnly = 3,  // the merges of INT4 partials (rows that mix both paths in heads with many flagged K blocks)
+};
+hipError_t launch_fp16_attention(const KProblem& kp, const AttnArgs& a, Fp16Rows rows, hipStream_t s);
 }  // namespace rotattn

@@ -361,7 +361,7 @@ __device__ __forceinline__ void rotate_quantize(const KProblem& kp, const QKOut&
     const float nsr = (sx > 0.f) ? se / sx : 0.f;
     const uint8_t flag = (nsr > kp.tau) ? 1 : 0;
     (tensor ? o.k_flag : o.q_flag)[bi] = flag;
-    if (tensor == 1 && flag) atomicOr(&o.head_kflag[b * kp.H + h], 1u);
+    if (tensor == 1 && flag) atomicAdd(&o.head_kflag[b * kp.H + h], 1u);   // flagged K blocks of the head
   }
 }
 

@@ -99,7 +99,8 @@ int derive(const rotattn_problem* p, Derived* d) {
 
 // Workspace carve-up of every call. Offsets are 256-byte aligned.
 struct Layout {
-  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0, img = 0, vt = 0;
+  size_t tab = 0, absmax = 0, vcodes = 0, vscale = 0, vcolsum = 0, po = 0, pm = 0, pl = 0, qr = 0, kr = 0, img = 0,
+         vt = 0;
   size_t total = 0;
 };
 
@@ -119,7 +120,10 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
   const size_t pm_b = (size_t)BH * d.Lp * sizeof(float);
   const size_t rope_b = (size_t)BH * p->L * p->D * 2;
   const size_t img_b = (size_t)BH * d.NB * kv_image_bytes((int)d.Dp, p->D);
-  const size_t vt_b = (size_t)BH * d.NB * 128 * p->D;
+  const size_t vt_b = (size_t)BH * d.NB * f16_vt_bytes(p->D);
+  // the V^T blocks only when the FP16 path can run: block routing on, or a head mask passed
+  const bool fp16 = routes(p) || call == ROTATTN_CALL_ATTENTION_HEAD_FALLBACK ||
+                    call == ROTATTN_CALL_FORWARD_HEAD_FALLBACK;
   switch (call) {
     case ROTATTN_CALL_QUANTIZE_QK:
       L.tab = take(tab_bytes);
@@ -128,15 +132,17 @@ Layout layout(const rotattn_problem* p, const Derived& d, int call) {
       L.absmax = take(absmax_b);
       break;
     case ROTATTN_CALL_ATTENTION:
+    case ROTATTN_CALL_ATTENTION_HEAD_FALLBACK:
       L.img = take(img_b);
-      L.vt = take(vt_b);
+      if (fp16) L.vt = take(vt_b);
       if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
       break;
     case ROTATTN_CALL_FORWARD:
+    case ROTATTN_CALL_FORWARD_HEAD_FALLBACK:
       L.vcodes = take(vcodes_b); L.vscale = take(vscale_b); L.vcolsum = take(vcolsum_b);
       L.absmax = take(absmax_b);
       L.img = take(img_b);
-      L.vt = take(vt_b);
+      if (fp16) L.vt = take(vt_b);
       if (routes(p)) { L.po = take(po_b); L.pm = take(pm_b); L.pl = take(pm_b); }
       break;
     case ROTATTN_CALL_FP16_FORWARD:
@@ -185,6 +191,44 @@ int check_v(const rotattn_v_buffers* vq) {
   return ROTATTN_OK;
 }
 
+// One side stream (default priority, non-blocking) and a fork and a join
+// event per device, created on the first call that needs them and kept until
+// the process ends; the mutex keeps the record/wait sequences of concurrent
+// calls on one device from interleaving.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream* g_side[kMaxSideDevices] = {};
+
+int side_stream(hipStream_t s, SideStream** out) {
+  int dev = -1;
+  if (s != nullptr) {
+    if (hipStreamGetDevice(s, &dev) != hipSuccess) return ROTATTN_EINVAL;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return ROTATTN_ELAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxSideDevices) return ROTATTN_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (g_side[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ROTATTN_ELAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ROTATTN_ELAUNCH;
+    SideStream* ss = new SideStream();
+    const bool ok = hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) == hipSuccess;
+    if (cur != dev) hipSetDevice(cur);
+    if (!ok) return ROTATTN_ELAUNCH;
+    g_side[dev] = ss;
+  }
+  *out = g_side[dev];
+  return ROTATTN_OK;
+}
+
 int attention_impl(const rotattn_problem* p, const Derived& d, const rotattn_qk_buffers* qk,
                    const rotattn_v_buffers* vq, const void* v, const uint8_t* head_fallback, void* out,
                    void* ws, const Layout& L, hipStream_t s) {
@@ -207,12 +251,29 @@ int attention_impl(const rotattn_problem* p, const Derived& d, const rotattn_qk_
   a.kv_image = img;
   int rc = launched(launch_kv_image(d.kp, a, img, s));
   if (rc != ROTATTN_OK) return rc;
-  rc = launched(launch_int4_attention(d.kp, a, false, s));
-  if (rc != ROTATTN_OK || !fp16_needed) return rc;
-  uint8_t* vt = at<uint8_t>(ws, L.vt);
-  a.f16_vt = vt;
-  if ((rc = launched(launch_fp16_vt(d.kp, a.v, vt, s))) != ROTATTN_OK) return rc;
-  return launched(launch_fp16_attention(d.kp, a, false, s));
+  if (fp16_needed) {   // V^T blocks of the FP16 tiles, which both kernels read
+    uint8_t* vt = at<uint8_t>(ws, L.vt);
+    a.f16_vt = vt;
+    if ((rc = launched(launch_fp16_vt(d.kp, a.v, vt, s))) != ROTATTN_OK) return rc;
+  }
+  if (!fp16_needed) return launched(launch_int4_attention(d.kp, a, false, s));
+  // Rows that run whole on FP16 do not depend on the INT4 rows: they go to the
+  // device's side stream, forked from and joined back into the caller's
+  // stream, so that the two kernels share the machine. The INT4 rows (rows
+  // that mix both paths: their FP16 tiles too, or, in heads with many flagged
+  // K blocks, their INT4 partials), then the merges of those partials, stay
+  // on the caller's stream.
+  SideStream* ss = nullptr;
+  if ((rc = side_stream(s, &ss)) != ROTATTN_OK) return rc;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+    return ROTATTN_ELAUNCH;
+  if ((rc = launched(launch_fp16_attention(d.kp, a, kFp16FullOnly, ss->stream))) != ROTATTN_OK) return rc;
+  if ((rc = launched(launch_int4_attention(d.kp, a, false, s))) != ROTATTN_OK) return rc;
+  if (route && (rc = launched(launch_fp16_attention(d.kp, a, kFp16MergeOnly, s))) != ROTATTN_OK) return rc;
+  if (hipEventRecord(ss->join, ss->stream) != hipSuccess || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess)
+    return ROTATTN_ELAUNCH;
+  return ROTATTN_OK;
 }
 
 int check_attention_args(const rotattn_problem* p, const rotattn_qk_buffers* qk, const void* v,
@@ -328,7 +389,7 @@ int rotattn_workspace_bytes(const rotattn_problem* p, int call, size_t* bytes) {
   Derived d;
   const int rc = derive(p, &d);
   if (rc != ROTATTN_OK) return rc;
-  if (bytes == nullptr || call < 0 || call > ROTATTN_CALL_SPARSE_ATTENTION) return ROTATTN_EINVAL;
+  if (bytes == nullptr || call < 0 || call > ROTATTN_CALL_FORWARD_HEAD_FALLBACK) return ROTATTN_EINVAL;
   *bytes = layout(p, d, call).total;
   return ROTATTN_OK;
 }
@@ -387,7 +448,7 @@ int rotattn_attention(const rotattn_problem* p, const rotattn_qk_buffers* qk, co
   if ((rc = check_qk(qk)) != ROTATTN_OK) return rc;
   if ((rc = check_v(vq)) != ROTATTN_OK) return rc;
   if ((rc = check_attention_args(p, qk, v, head_fallback, out)) != ROTATTN_OK) return rc;
-  const Layout L = layout(p, d, ROTATTN_CALL_ATTENTION);
+  const Layout L = layout(p, d, head_fallback ? ROTATTN_CALL_ATTENTION_HEAD_FALLBACK : ROTATTN_CALL_ATTENTION);
   if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
   if (p->L == 0) return ROTATTN_OK;
   return attention_impl(p, d, qk, vq, v, head_fallback, out, workspace, L, static_cast<hipStream_t>(stream));
@@ -404,7 +465,7 @@ int rotattn_forward(const rotattn_problem* p, const rotattn_qk_buffers* qk, cons
   if (v == nullptr) return ROTATTN_EINVAL;
   if (!aligned16(v)) return ROTATTN_EALIGN;
   if ((rc = check_attention_args(p, qk, v, head_fallback, out)) != ROTATTN_OK) return rc;
-  const Layout L = layout(p, d, ROTATTN_CALL_FORWARD);
+  const Layout L = layout(p, d, head_fallback ? ROTATTN_CALL_FORWARD_HEAD_FALLBACK : ROTATTN_CALL_FORWARD);
   if ((rc = check_ws(L, workspace, workspace_bytes)) != ROTATTN_OK) return rc;
   if (p->L == 0) return ROTATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -442,7 +503,7 @@ int rotattn_fp16_forward(const rotattn_problem* p, const void* q, const void* k,
   uint8_t* vt = at<uint8_t>(workspace, L.vt);
   a.f16_vt = vt;
   if ((rc = launched(launch_fp16_vt(d.kp, a.v, vt, s))) != ROTATTN_OK) return rc;
-  return launched(launch_fp16_attention(d.kp, a, true, s));
+  return launched(launch_fp16_attention(d.kp, a, kFp16WholeCall, s));
 }
 
 int rotattn_debug_dump(const rotattn_problem* p, const rotattn_qk_buffers* qk, const rotattn_v_buffers* vq,

@@ -67,16 +67,23 @@ def test_sizes_720p():
     # 12288-byte form (64 K rows and 128 V rows of 24-byte FP6 slots, 4 and 2 slots per row)
     img = 40 * 1182 * 12288
     vt = 40 * 1182 * 64 * 128 * 2   # transposed fp16 V blocks of the FP16 path
-    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img + vt
+    # without routing and without a head mask the FP16 path cannot run: no V^T blocks
+    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION) == img
+    assert Bd.workspace_bytes(p, Bd.CALL_ATTENTION_HEAD_FALLBACK) == img + vt
+    assert Bd.workspace_bytes(p, Bd.CALL_FORWARD_HEAD_FALLBACK) - Bd.workspace_bytes(p, Bd.CALL_FORWARD) == vt
     assert Bd.workspace_bytes(p, Bd.CALL_DEBUG_DUMP) == img
     assert Bd.workspace_bytes(p, Bd.CALL_SPARSE_ATTENTION) == img
     # block-sparse mask: one row per 128 query rows, ceil(1182 / 32) = 37 words per row
     assert (s.mask_rows, s.mask_words, s.mask_bytes) == (591, 37, 40 * 591 * 37 * 4)
     assert s.bsum_bytes == 40 * 1182 * 128 * 4
-    # partial buffers on top only when block routing is on
+    # with block routing: the V^T blocks with or without a head mask, and the INT4 partial results of rows
+    # that mix both paths (float32 O [Lp, D] and m, l [Lp] per head)
     pm = Bd.problem_from_workload(W.WORKLOADS["mixed"])
     img_m = 12 * 512 * 16384   # D' = 192: dense, 64 x 6 + 128 x 2 slots of 24 bytes (15360), padded to 16384
-    assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) >= img_m + 12 * 512 * 64 * 128 * 2 + 12 * 32768 * 128 * 4
+    vt_m = 12 * 512 * 64 * 128 * 2
+    part = 12 * 32768 * 128 * 4 + 2 * 12 * 32768 * 4
+    assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION) == img_m + vt_m + part
+    assert Bd.workspace_bytes(pm, Bd.CALL_ATTENTION_HEAD_FALLBACK) == img_m + vt_m + part
 
 
 @pytest.mark.parametrize("kw,code", [

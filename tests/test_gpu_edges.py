@@ -265,3 +265,32 @@ def test_rope_tables_bitwise(name, w):
         assert np.array_equal(tab[off:off + cnt].view(np.uint32), c.ravel().view(np.uint32)), (name, a, "cos")
         assert np.array_equal(tab[off + cnt:off + 2 * cnt].view(np.uint32), s.ravel().view(np.uint32)), (name, a, "sin")
         off += 2 * cnt
+
+
+@pytest.mark.parametrize("n_flag", [3, 20])
+def test_mixed_rows_inline_and_merged(n_flag):
+    """Rows that mix both paths, in a head with few flagged K blocks (at most 16: the INT4 kernel finishes their
+    FP16 tiles after its loop) and in one with many (the FP16 kernel merges the INT4 partials): planted
+    high-norm key tokens flag n_flag K blocks of head 0; head 1 is masked; outputs against the oracle."""
+    G.require_gpu()
+    w = W.WORKLOADS["mixed"].replace(H=2, grid=(1, 40, 64))      # L = 2560, NB = 40
+    x = W.full_inputs(w)
+    rng = np.random.default_rng(n_flag)
+    blocks = rng.choice(40, size=n_flag, replace=False)
+    for j in blocks:
+        x["k"][0, 0, 64 * j + 17] *= np.float16(14)
+    print(f"[gpu] mixed rows: {n_flag} planted K blocks L={w.L}", flush=True)
+    p = G.R.problem_from_workload(w, tau=0.05)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    mask = np.array([0, 1], dtype=np.uint8)
+    out = G.host(G.R.rotattn_forward(p, qk, v, head_fallback=G.dev(mask))).astype(np.float64)
+    kf = G.host(qk.k_flag)[0, 0].astype(bool)
+    assert kf.sum() >= n_flag and (kf.sum() > 16) == (n_flag > 16), int(kf.sum())
+    assert int(G.host(qk.head_kflag)[0]) == int(kf.sum())          # the head's count of flagged K blocks
+    for h in range(2):
+        o = G.oracle_head(w, x, 0, h, tau=0.05, head_masked=bool(mask[h]),
+                          q_flags=G.host(qk.q_flag)[0, h].astype(bool), k_flags=G.host(qk.k_flag)[0, h].astype(bool))
+        tol = G.head_output_tol(w, x, 0, h, o, bool(mask[h]))
+        err = np.abs(out[0, h] - o["out"])
+        assert (err <= tol).all(), (h, float(err.max()))

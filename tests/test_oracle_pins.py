@@ -502,6 +502,43 @@ def _head(name="tiny", h=0, L=None):
     return w, W.head_inputs(w, 0, h)
 
 
+def test_merge_equals_continued_recurrence():
+    """Continuing the online softmax (RainFusion2.0 sec. 3.1) over the FP16 key blocks from the INT4 loop's final
+    state (m, l, O in V's units) gives the log-sum-exp merge of the two partials: the order in which a row with
+    both paths is finished does not change the oracle's result (float64, to 1e-12)."""
+    rng = _rng(41)
+    L, D = 300, 64
+    q = rng.standard_normal((L, D)).astype(np.float16)
+    k = rng.standard_normal((L, D)).astype(np.float16)
+    v = rng.standard_normal((L, D)).astype(np.float16)
+    grid, split = (1, 10, 30), (22, 21, 21)
+    qp = O.qk_prologue(q, 0, grid, split, 10000.0, O.ROT_FULL)
+    kp = O.qk_prologue(k, 0, grid, split, 10000.0, O.ROT_FULL)
+    vc, sv, cs = O.quantize_v(v)
+    fk = np.array([False, True, False, False, True])
+    rows = np.arange(0, L, 3)
+    p1 = O.int4_flash_rows(qp["codes"], qp["scale"], kp["codes"], kp["scale"], vc, sv, cs, L, D, rows,
+                           key_blocks=~fk)
+    p2 = O.fp16_rows(qp["rope16"], kp["rope16"], v, L, D, rows, key_blocks=fk)
+    want = O.merge(p1["O_scaled"], p1["m"], p1["l"], p2["O"], p2["m"], p2["l"])
+    # the continuation, block by block in ascending order
+    m = p1["m"].astype(np.float64).copy()
+    lsum = p1["l"].copy()
+    acc = p1["O_scaled"].copy()
+    c = math.log2(math.e) / math.sqrt(D)
+    qq = qp["rope16"][rows].astype(np.float64)
+    for j in np.nonzero(fk)[0]:
+        keys = np.arange(64 * j, min(64 * j + 64, L))
+        S2 = (qq @ kp["rope16"][keys].astype(np.float64).T) * c
+        m_new = np.maximum(m, S2.max(axis=1))
+        alpha = np.exp2(m - m_new)
+        P = np.exp2(S2 - m_new[:, None])
+        acc = alpha[:, None] * acc + P @ v[keys].astype(np.float64)
+        lsum = alpha * lsum + P.sum(axis=1)
+        m = m_new
+    assert np.allclose(acc / lsum[:, None], want, rtol=1e-12, atol=1e-13)
+
+
 def test_routing_all_fp16_equals_fp16_forward():
     """A masked head runs every tile on the FP16 path: identical to the whole-call FP16 forward."""
     w, x = _head()
