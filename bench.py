@@ -167,7 +167,7 @@ def main():
     ap.add_argument("--workload", default="720p", choices=list(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="time bound of the oracle baseline sample (whole 512-row chunks)")
+                    help="time bound of the oracle baseline sample (whole 256-row chunks per worker)")
     ap.add_argument("--sparse", type=float, default=None, metavar="F",
                     help="block-sparse path keeping the top round(F * NB) key blocks per 128-row query block")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
