@@ -7,6 +7,8 @@ the calls raise: there is no fallback.
 from __future__ import annotations
 
 import ctypes as C
+import functools
+import inspect
 import math
 import os
 from dataclasses import dataclass
@@ -165,6 +167,22 @@ def _stream(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run an entry point with the caller's `stream` (if given) as torch's current stream, so that the
+    buffers the binding allocates for the call (workspace, outputs) belong to that stream: the caching
+    allocator then reuses a freed workspace only for work ordered after the call on the same stream."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        s = sig.bind(*args, **kwargs).arguments.get("stream")
+        if s is None:
+            return fn(*args, **kwargs)
+        with _torch().cuda.stream(s):
+            return fn(*args, **kwargs)
+    return wrapped
+
+
 def _workspace(p: Problem, call: int, device, ws=None):
     torch = _torch()
     n = workspace_bytes(p, call)
@@ -249,6 +267,7 @@ def alloc_v(p: Problem, device) -> VCodes:
     )
 
 
+@_on_stream
 def rotattn_quantize_qk(p: Problem, q, k, out: QKCodes = None, rope_copy: bool = False, ws=None, stream=None,
                         block_sums: bool = False):
     """RoPE + rotation + per-block INT4 quantization of Q and K (see include/rotattn.h); block_sums also writes
@@ -262,6 +281,7 @@ def rotattn_quantize_qk(p: Problem, q, k, out: QKCodes = None, rope_copy: bool =
     return out
 
 
+@_on_stream
 def rotattn_quantize_qk_static(p: Problem, q, k, out: QKCodes = None, rope_copy: bool = False, stream=None,
                                block_sums: bool = False):
     """rotattn_quantize_qk with the library's static scratch instead of a workspace (no device allocation inside
@@ -274,6 +294,7 @@ def rotattn_quantize_qk_static(p: Problem, q, k, out: QKCodes = None, rope_copy:
     return out
 
 
+@_on_stream
 def rotattn_quantize_v(p: Problem, v, out: VCodes = None, ws=None, stream=None):
     if out is None:
         out = alloc_v(p, v.device)
@@ -284,6 +305,7 @@ def rotattn_quantize_v(p: Problem, v, out: VCodes = None, ws=None, stream=None):
     return out
 
 
+@_on_stream
 def rotattn_attention(p: Problem, qk: QKCodes, vq: VCodes, v=None, head_fallback=None, out=None, ws=None,
                       stream=None):
     torch = _torch()
@@ -297,6 +319,7 @@ def rotattn_attention(p: Problem, qk: QKCodes, vq: VCodes, v=None, head_fallback
     return out
 
 
+@_on_stream
 def rotattn_forward(p: Problem, qk: QKCodes, v, head_fallback=None, out=None, ws=None, stream=None):
     torch = _torch()
     if out is None:
@@ -308,6 +331,7 @@ def rotattn_forward(p: Problem, qk: QKCodes, v, head_fallback=None, out=None, ws
     return out
 
 
+@_on_stream
 def rotattn_fp16_forward(p: Problem, q, k, v, out=None, ws=None, stream=None):
     torch = _torch()
     if out is None:
@@ -318,6 +342,7 @@ def rotattn_fp16_forward(p: Problem, q, k, v, out=None, ws=None, stream=None):
     return out
 
 
+@_on_stream
 def rotattn_block_mask(p: Problem, qk: QKCodes, topn: int, out=None, ws=None, stream=None):
     """Block-sparse mask from the block sums of rotattn_quantize_qk(block_sums=True) (see include/rotattn.h):
     int32 view of uint32 [B, H, mask_rows, mask_words], one row per 128 query rows."""
@@ -333,6 +358,7 @@ def rotattn_block_mask(p: Problem, qk: QKCodes, topn: int, out=None, ws=None, st
     return out
 
 
+@_on_stream
 def rotattn_sparse_attention(p: Problem, qk: QKCodes, vq: VCodes, block_mask, out=None, ws=None, stream=None):
     """Block-sparse INT4 attention over the key blocks `block_mask` keeps (see include/rotattn.h)."""
     torch = _torch()
@@ -355,6 +381,7 @@ def mask_to_bool(mask_words, NB: int):
     return bits.reshape(w.shape[:-1] + (w.shape[-1] * 32,))[..., :NB].astype(bool)
 
 
+@_on_stream
 def rotattn_debug_dump(p: Problem, qk: QKCodes, vq: VCodes, units, head_fallback=None, ws=None, stream=None,
                        block_mask=None, p15: bool = True):
     """Intermediate integers of the INT4 kernel for 64-row query blocks `units` ((b*H+h)*NB + block), and (p15)

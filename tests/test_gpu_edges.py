@@ -294,3 +294,36 @@ def test_mixed_rows_inline_and_merged(n_flag):
         tol = G.head_output_tol(w, x, 0, h, o, bool(mask[h]))
         err = np.abs(out[0, h] - o["out"])
         assert (err <= tol).all(), (h, float(err.max()))
+
+
+def test_routed_call_on_user_stream():
+    """A call that routes rows to FP16 forks the library's side stream from the caller's stream and joins it back
+    before returning. On a non-default stream, with the output buffer filled with NaN first and read back by a
+    copy on that stream, synchronizing that stream alone must expose the whole output, bit-identical to the same
+    call on the default stream, on each of three calls. Head 0 has 18 flagged K blocks (merge), head 2 three
+    (inline), heads 1 and 3 are masked (whole-row FP16)."""
+    G.require_gpu()
+    w = W.WORKLOADS["mixed"].replace(H=4, grid=(1, 40, 64))      # L = 2560, NB = 40
+    x = W.full_inputs(w)
+    for j in (2, 3, 5, 7, 9, 11, 13, 17, 19, 21, 23, 25, 27, 29, 31, 33, 35, 37):
+        x["k"][0, 0, 64 * j + 17] *= np.float16(14)
+    for j in (4, 14, 24):
+        x["k"][0, 2, 64 * j + 40] *= np.float16(14)
+    print(f"[gpu] routed call on a user stream L={w.L}", flush=True)
+    p = G.R.problem_from_workload(w, tau=0.05)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    m = G.dev(np.array([0, 1, 0, 1], dtype=np.uint8))
+    kcount = G.host(qk.head_kflag)
+    assert kcount[0] > 16 and 0 < kcount[2] <= 16, kcount
+    ref = G.host(G.R.rotattn_forward(p, qk, v, head_fallback=m))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            out = torch.full((w.B, w.H, w.L, w.D), float("nan"), dtype=torch.float16, device="cuda")
+            G.R.rotattn_forward(p, qk, v, head_fallback=m, out=out, stream=s)
+            host = torch.empty(out.shape, dtype=out.dtype, pin_memory=True)
+            host.copy_(out, non_blocking=True)
+        s.synchronize()
+        assert np.array_equal(host.numpy().view(np.uint16), ref.view(np.uint16)), rep
