@@ -327,3 +327,43 @@ def test_routed_call_on_user_stream():
             host.copy_(out, non_blocking=True)
         s.synchronize()
         assert np.array_equal(host.numpy().view(np.uint16), ref.view(np.uint16)), rep
+
+
+def test_routed_call_graph_replay():
+    """The routed forward (side-stream fork and join, inline and merged mixed rows, masked heads) captured in a
+    HIP graph through torch's stream capture: every replay, with the output filled with NaN before it and an
+    eager call of the library between replays, equals the eager result bit for bit."""
+    G.require_gpu()
+    w = W.WORKLOADS["mixed"].replace(H=4, grid=(1, 40, 64))      # L = 2560, NB = 40
+    x = W.full_inputs(w)
+    for j in (2, 3, 5, 7, 9, 11, 13, 17, 19, 21, 23, 25, 27, 29, 31, 33, 35, 37):
+        x["k"][0, 0, 64 * j + 17] *= np.float16(14)
+    for j in (4, 14, 24):
+        x["k"][0, 2, 64 * j + 40] *= np.float16(14)
+    print(f"[gpu] routed call in a graph L={w.L}", flush=True)
+    p = G.R.problem_from_workload(w, tau=0.05)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    m = G.dev(np.array([0, 1, 0, 1], dtype=np.uint8))
+    ref = G.host(G.R.rotattn_forward(p, qk, v, head_fallback=m))
+    n = G.R.workspace_bytes(p, G.R.binding.CALL_FORWARD_HEAD_FALLBACK)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.H, w.L, w.D), dtype=torch.float16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                                 # warm-up on the capture's kind of stream
+        G.R.rotattn_forward(p, qk, v, head_fallback=m, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.R.rotattn_forward(p, qk, v, head_fallback=m, out=out, ws=ws)
+    other = torch.empty_like(out)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), ref.view(np.uint16)), rep
+        G.R.rotattn_forward(p, qk, v, head_fallback=m, out=other)   # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(other.cpu().numpy().view(np.uint16), ref.view(np.uint16)), rep
