@@ -231,6 +231,37 @@ def test_all_heads_masked_equals_fp16_forward():
     assert np.array_equal(a.view(np.uint16), bb.view(np.uint16))
 
 
+def test_tau_zero_equals_fp16_forward():
+    """tau = 0 flags every block with any energy, so every row runs whole on FP16 through the Q flags (the
+    routing path, not the head mask): identical bits to the whole-call FP16 forward."""
+    G.require_gpu()
+    w = CASES["ragged_prefix"]
+    x = W.full_inputs(w)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    p = G.R.problem_from_workload(w, tau=0.0)
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    assert G.host(qk.q_flag).all() and G.host(qk.k_flag).all()
+    a = G.host(G.R.rotattn_forward(p, qk, v))
+    bb = G.host(G.R.rotattn_fp16_forward(G.R.problem_from_workload(w), q, k, v))
+    assert np.array_equal(a.view(np.uint16), bb.view(np.uint16))
+
+
+def test_routing_without_flags_equals_unrouted():
+    """A finite tau that flags nothing switches block routing on (the routed INT4 instance, the side stream)
+    with nothing to route: identical bits to the call with routing off."""
+    G.require_gpu()
+    w = CASES["ragged_prefix"]
+    x = W.full_inputs(w)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    p_on = G.R.problem_from_workload(w, tau=1e30)
+    qk_on = G.R.rotattn_quantize_qk(p_on, q, k, rope_copy=True)
+    assert not G.host(qk_on.q_flag).any() and not G.host(qk_on.k_flag).any()
+    a = G.host(G.R.rotattn_forward(p_on, qk_on, v))
+    p_off = G.R.problem_from_workload(w)
+    b_ = G.host(G.R.rotattn_forward(p_off, G.R.rotattn_quantize_qk(p_off, q, k), v))
+    assert np.array_equal(a.view(np.uint16), b_.view(np.uint16))
+
+
 def test_determinism():
     """Two runs give bitwise-equal outputs and dumps."""
     G.require_gpu()
