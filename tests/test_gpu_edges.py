@@ -84,6 +84,20 @@ def test_mask_and_block_rule_small():
     _run_and_check(w, x, tau=0.05, head_mask=mask)
 
 
+def test_routing_strided_batch():
+    """The mask and the block rule with B = 2 in tokens-major [B, L, H, D] storage: masked heads in both batch
+    entries, planted high-norm key tokens flagging K blocks in a head of the second entry (its rows mix both
+    paths) and a flagged Q block in the first; every head against the oracle."""
+    G.require_gpu()
+    w = W.WORKLOADS["mixed"].replace(B=2, H=3, grid=(2, 9, 15))    # L = 270: five key blocks, ragged
+    x = W.full_inputs(w)
+    x["k"][1, 2, 70] *= np.float16(12)
+    x["k"][1, 2, 200] *= np.float16(12)
+    x["q"][0, 0, 5] *= np.float16(12)
+    mask = np.array([0, 1, 0, 0, 0, 1], dtype=np.uint8)
+    _run_and_check(w, x, layout="blhd", tau=0.05, head_mask=mask)
+
+
 def test_empty_problem():
     """L = 0: every call returns success and touches nothing."""
     G.require_gpu()
