@@ -15,7 +15,10 @@ codes are exact in E2M3), whose dense peak is derived from the device:
 CUs x engine clock x 16384 ops per CU and clock (4 SIMDs, one 32x32x64
 product of 131072 ops every 32 cycles each); 10.07 POP/s at 256 CUs and
 2.4 GHz. `achieved` counts the operations the kernel executes, 2 (D' + D)
-per score element (D' = 192 for the per-group rotation). The CPU baseline is
+per score element (D' = 192 for the per-group rotation). The kernel is in fact
+bound by its vector ALU (the float32 softmax of every score), which caps the
+products well below that peak; `valu_busy` carries rocprof's VALUBusy of the
+kernel from the committed profile of the workload. The CPU baseline is
 the oracle (numpy) on a bounded sample of the same workload, over the host's
 cores; the same leg reports the fidelity of the GPU output (cosine
 similarity to exact float64 attention on sampled rows).
@@ -66,14 +69,15 @@ def device_peak():
 KERNEL_SOURCES = ("int4_quantized_flashattention_amd/csrc/attn_int4.hip", "int4_quantized_flashattention_amd/csrc/common.h")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the INT4 attention kernel, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary of this workload (calibrated against a plain copy), or None when there is none or the kernel
+def profiled(workload: str) -> dict:
+    """Per-launch figures of the INT4 attention kernel from the committed rocprofv3 summary of this workload
+    (`profiles/int4_attn_kernel_<workload>.md`, its "- key: value" lines): HBM traffic from FETCH_SIZE /
+    WRITE_SIZE calibrated against a plain copy, and VALUBusy. Empty when there is no summary or the kernel
     sources have changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"int4_attn_kernel_{workload}.md")
     if not os.path.exists(path):
-        return None
+        return {}
     vals = {}
     for line in open(path):
         if line.startswith("- ") and ": " in line:
@@ -83,9 +87,21 @@ def measured_traffic(workload: str):
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if vals.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
-        return None
-    return int(vals["traffic_bytes_per_launch"])
+    if vals.get("kernel_source_sha256") != h.hexdigest():
+        return {}
+    return vals
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the INT4 attention kernel (profiled), or None."""
+    v = profiled(workload).get("traffic_bytes_per_launch")
+    return int(v) if v is not None else None
+
+
+def measured_valu_busy(workload: str):
+    """rocprof's VALUBusy of the INT4 attention kernel (profiled), or None."""
+    v = profiled(workload).get("valu_busy")
+    return float(v) if v is not None else None
 
 
 def baseline_heads(w: W.Workload):
@@ -267,7 +283,10 @@ def main():
                      "avg_ms": round(att_ms, 4), "mfma_dtype": "fp6 e2m3 (v_mfma_scale_f32_32x32x64_f8f6f4)",
                      "peak_derivation": f"{cus} CUs x {ghz:.3f} GHz x {FP6_OPS_PER_CU_CLK} ops per CU-clock",
                      "peak_published": FP6_PEAK_PUBLISHED_TOPS,
-                     "executed_ops_per_score": 2 * (w.Dp + w.D)},
+                     "executed_ops_per_score": 2 * (w.Dp + w.D),
+                     # the unit that binds the kernel: the per-score float32 softmax keeps the vector ALU
+                     # this busy (profiled; null once the kernel sources change), which caps the matrix cores
+                     "valu_busy": measured_valu_busy(w.name)},
         "int8_peak_share": round(credited_rate / INT8_PEAK_TOPS, 4),
         "credited_attention_TOPS": round(credited_rate, 3),
         "breakdown_ms": {"quantize_qk": round(float(t_qk.mean()), 4), "quantize_v": round(float(t_v.mean()), 4),
