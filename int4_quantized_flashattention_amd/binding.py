@@ -14,7 +14,8 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librotattn.so")
+# ROTATTN_LIBRARY: another build of the same library (e.g. one with host-side sanitizers)
+LIB_PATH = os.environ.get("ROTATTN_LIBRARY") or os.path.join(HERE, "librotattn.so")
 
 ROT_FULL = 0
 ROT_GROUP64 = 1

@@ -221,8 +221,17 @@ int side_stream(hipStream_t s, SideStream** out) {
     const bool ok = hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking) == hipSuccess &&
                     hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) == hipSuccess &&
                     hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) == hipSuccess;
-    if (cur != dev) hipSetDevice(cur);
-    if (!ok) return ROTATTN_ELAUNCH;
+    if (!ok) {   // release what was created
+      if (ss->join != nullptr) (void)hipEventDestroy(ss->join);
+      if (ss->fork != nullptr) (void)hipEventDestroy(ss->fork);
+      if (ss->stream != nullptr) (void)hipStreamDestroy(ss->stream);
+      delete ss;
+    }
+    const bool restored = cur == dev || hipSetDevice(cur) == hipSuccess;
+    if (!ok || !restored) {
+      if (ok) g_side[dev] = ss;   // created: keep it for the next call
+      return ROTATTN_ELAUNCH;
+    }
     g_side[dev] = ss;
   }
   *out = g_side[dev];
