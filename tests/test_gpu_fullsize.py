@@ -1,6 +1,6 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
-For each workload (480p, small head dim with text prefix, mixed precision,
+For each workload (tiny, 480p, small head dim with text prefix, mixed precision,
 720p) the whole path runs on the GPU exactly as the benchmark runs it
 (rotattn_quantize_qk, rotattn_quantize_v, rotattn_attention). Sampled heads
 are then checked against the oracle: their Q/K/V codes, scales and flags in
@@ -23,7 +23,7 @@ from tests import gpu_common as G
 torch = G.torch
 pytestmark = pytest.mark.gpu
 
-FULL = ["480p", "smalld", "mixed", "720p"]
+FULL = ["tiny", "480p", "smalld", "mixed", "720p"]
 
 
 def _sample_blocks(NB, n):
