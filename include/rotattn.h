@@ -19,7 +19,11 @@
  *    rotattn_workspace_bytes), except for rotattn_quantize_qk_static, which
  *    uses a static device buffer of the library (see there).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
- *    null stream). No call synchronizes with the host.
+ *    null stream). No call synchronizes with the host. A call enqueues kernels
+ *    and event records only (no memsets or copies), so it can be captured in
+ *    a HIP graph; the calls that can route rows to FP16 fork a library-owned
+ *    side stream from `stream` with an event and join it back before they
+ *    return, so all of their work is ordered before later work on `stream`.
  *  - Return ROTATTN_OK (0) on success or a negative ROTATTN_E* code.
  *    Argument errors are detected on the host before anything is enqueued
  *    and leave every output untouched. ROTATTN_ELAUNCH reports a failed
