@@ -92,7 +92,8 @@ def _sparse_tol(w, o, rows, M):
 
 
 CASES = [("tiny", {}, 2), ("smalld", dict(H=2), 56), ("480p", dict(H=2), 102),
-         ("smalld", dict(H=2, split=(22, 22, 20)), 56)]   # even groups: block sums from the register prologue
+         ("smalld", dict(H=2, split=(22, 22, 20)), 56),   # even groups: block sums from the register prologue
+         ("tiny", dict(rotation=W.ROT_PAIR, grid=(3, 9, 15), prefix=5), 3)]   # mergeable rotation, ragged
 
 
 @pytest.mark.parametrize("name,kw,topn", CASES)
@@ -126,9 +127,13 @@ def test_sparse_mask_and_attention(name, kw, topn):
     cnt = np.minimum(64, L - 64 * np.arange(NB)).astype(np.float64)[:, None]
     for h in range(w.H):
         # block sums of the RoPE'd rows from the Q/K prologue
+        # (with the mergeable rotation, of the RoPE'd rows with the pair rotation folded in, as the
+        # prologue holds them; S_hat is the same, the rotation being orthogonal and shared by Q and K)
+        phase = O.pair_phase() if w.rotation == W.ROT_PAIR else 0.0
         for t in ("q", "k"):
-            want = O.block_means(x[t][0, h], w.prefix, w.grid, w.split, w.base, 64) * cnt
-            xr = np.abs(O.apply_rope(x[t][0, h].astype(np.float32), w.prefix, w.grid, w.split, w.base))
+            r32 = O.apply_rope(x[t][0, h].astype(np.float32), w.prefix, w.grid, w.split, w.base, phase)
+            want = np.add.reduceat(r32.astype(np.float64), np.arange(0, L, 64), axis=0)
+            xr = np.abs(r32)
             bound = 64 * 2.0 ** -23 * np.add.reduceat(xr.astype(np.float64), np.arange(0, L, 64), axis=0)
             got = G.host(getattr(qk, f"{t}_bsum")[0, h]).astype(np.float64)
             assert (np.abs(got - want) <= bound + 1e-30).all(), (h, t)
