@@ -381,3 +381,49 @@ def test_routed_call_graph_replay():
         G.R.rotattn_forward(p, qk, v, head_fallback=m, out=other)   # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(other.cpu().numpy().view(np.uint16), ref.view(np.uint16)), rep
+
+
+def test_routed_calls_from_two_threads():
+    """Two host threads issue routed forwards on their own streams at the same time (the library's one side
+    stream per device and its fork/join events are shared under a lock): every output is bit-identical to the
+    serial result."""
+    import threading
+    G.require_gpu()
+    w = W.WORKLOADS["mixed"].replace(H=4, grid=(1, 40, 64))      # L = 2560, NB = 40
+    x = W.full_inputs(w)
+    for j in (2, 3, 5, 7, 9, 11, 13, 17, 19, 21, 23, 25, 27, 29, 31, 33, 35, 37):
+        x["k"][0, 0, 64 * j + 17] *= np.float16(14)
+    for j in (4, 14, 24):
+        x["k"][0, 2, 64 * j + 40] *= np.float16(14)
+    print(f"[gpu] routed calls from two threads L={w.L}", flush=True)
+    p = G.R.problem_from_workload(w, tau=0.05)
+    q, k, v = G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"])
+    qk = G.R.rotattn_quantize_qk(p, q, k, rope_copy=True)
+    m = G.dev(np.array([0, 1, 0, 1], dtype=np.uint8))
+    ref = G.host(G.R.rotattn_forward(p, qk, v, head_fallback=m)).view(np.uint16)
+    n = G.R.workspace_bytes(p, G.R.binding.CALL_FORWARD_HEAD_FALLBACK)
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+                outs = [torch.empty((w.B, w.H, w.L, w.D), dtype=torch.float16, device="cuda") for _ in range(5)]
+                for o in outs:
+                    G.R.rotattn_forward(p, qk, v, head_fallback=m, out=o, ws=ws, stream=s)
+            s.synchronize()
+            results[tid] = [o.cpu().numpy().view(np.uint16) for o in outs]
+        except Exception as e:   # reported below
+            errors.append(repr(e))
+
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for tid in range(2):
+        for i, o in enumerate(results[tid]):
+            assert np.array_equal(o, ref), (tid, i)
