@@ -191,7 +191,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is design only "
-                                   "(per-head split, see DESIGN.md)", "n_gpus": args.gpus}))
+                                   "(each GPU would take whole heads)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
