@@ -190,7 +190,7 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (scales HBM traffic counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is design only "
+        print(json.dumps({"error": "rotattn runs on one GPU; multi-GPU sharding is design only "
                                    "(each GPU would take whole heads)", "n_gpus": args.gpus}))
         sys.exit(2)
 
