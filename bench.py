@@ -105,8 +105,8 @@ def measured_valu_busy(workload: str):
 
 
 def baseline_heads(w: W.Workload):
-    """Heads of the CPU baseline, one per usable host core (the affinity mask, capped by OMP_NUM_THREADS, which
-    the GPU machines set to the host share of one GPU), spread evenly over the workload's heads."""
+    """Heads of the CPU baseline, one per usable host core (the affinity mask, capped by OMP_NUM_THREADS when
+    that is set, e.g. to the host cores that go with one GPU), spread evenly over the workload's heads."""
     cores = len(os.sched_getaffinity(0))
     cap = os.environ.get("OMP_NUM_THREADS")
     if cap and cap.isdigit():

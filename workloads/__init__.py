@@ -101,7 +101,7 @@ WORKLOADS = {
                      tau=math.inf, seed=1005),
 }
 
-# the order the workloads are listed in the task description
+# the workloads from the smallest to the largest
 WORKLOAD_ORDER = ["tiny", "480p", "smalld", "mixed", "720p"]
 
 
