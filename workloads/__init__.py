@@ -101,7 +101,7 @@ WORKLOADS = {
                      tau=math.inf, seed=1005),
 }
 
-# the workloads from the smallest to the largest
+# the order in which the workloads are reported
 WORKLOAD_ORDER = ["tiny", "480p", "smalld", "mixed", "720p"]
 
 
