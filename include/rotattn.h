@@ -4,8 +4,8 @@
  *
  * The method is the one the RotateAttention abstract (arXiv 2607.02584)
  * describes: 3D RoPE on Q and K, an orthonormal Walsh-Hadamard rotation
- * applied after RoPE (the "negligible-overhead" variant of its RoPE-aware
- * rotation), symmetric INT4 Q/K/V, a fused flash loop with integer Q.K^T,
+ * applied after RoPE (the variant of its RoPE-aware rotation that runs online
+ * at little cost), symmetric INT4 Q/K/V, a fused flash loop with integer Q.K^T,
  * float32 online softmax and the range-optimized P quantization (fixed scale
  * 1/15, zero-point -8), and selective FP16 fallback for accuracy-sensitive
  * blocks, heads and denoising steps. The flash loop follows the online-softmax

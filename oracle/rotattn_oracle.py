@@ -11,7 +11,7 @@ What it computes, step by step, in the pages' order:
      width frequency groups). Token order is frame-major [F, H, W]
      (RainFusion2.0, section "3D Window Permutation", default layout).
   2. A Walsh-Hadamard rotation applied after RoPE to Q and K (RotateAttention
-     abstract, "RoPE-aware Rotation", the negligible-overhead online variant),
+     abstract, "RoPE-aware Rotation": the variant applied online at little cost),
      or the mergeable variant folded into RoPE (pair_phase). Either rotation
      is orthonormal, so Q K^T is unchanged.
   3. Symmetric INT4 quantization of Q and K per 64-token block, and of V per
@@ -127,8 +127,8 @@ def rope_tables(grid, split, base: float, phase: float = 0.0):
 def pair_phase() -> float:
     """Angle of the mergeable RoPE-aware rotation (RotateAttention abstract, "RoPE-aware Rotation").
 
-    Reading: the abstract names "mergeable rotation matrices that can be
-    fused into RoPE" without constructing them. An orthogonal R can be merged
+    Reading: the abstract names rotation matrices that can be merged into
+    RoPE but does not construct them. An orthogonal R can be merged
     into RoPE (RoPE_pos(x) R = RoPE_pos(x R) for every position, so R can be
     folded into the Q/K projections or into RoPE's tables) exactly when it
     commutes with every 3D-RoPE rotation; with the distinct frequencies of an
@@ -560,9 +560,9 @@ def sparse_block_mask(s_hat, topn: int, L: int, prefix: int, grid, bq: int = SPA
     """Block mask M [ceil(L/bq), ceil(L/bk)] of the block-sparse flash loop (RainFusion2.0 sections 3.1, 3.2, 3.4).
 
     M[i, j] = 1 for the topn key blocks j with the largest S_hat[i, j]
-    (reading of "the top-n important blocks K_j for each block Q_i"; the
-    page's "TopN(S_hat, dim=0)" is read as per query block; equal scores are
-    taken in ascending j), then the first-frame sink on top: every key block
+    (the page selects the n most important key blocks for each query block;
+    its top-n over dimension 0 of S_hat is read the same way, per query block;
+    equal scores are taken in ascending j), then the first-frame sink on top: every key block
     that holds a sink token is kept for every query block, and every query
     block that holds a sink token keeps every key block.
     """
