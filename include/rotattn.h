@@ -7,8 +7,8 @@
  * applied after RoPE (the variant of its RoPE-aware rotation that runs online
  * at little cost), symmetric INT4 Q/K/V, a fused flash loop with integer Q.K^T,
  * float32 online softmax and the range-optimized P quantization (fixed scale
- * 1/15, zero-point -8), and selective FP16 fallback for accuracy-sensitive
- * blocks, heads and denoising steps. The flash loop follows the online-softmax
+ * 1/15, zero-point -8), and an FP16 path for the blocks, heads and denoising
+ * steps where INT4 would lose too much accuracy. The flash loop follows the online-softmax
  * recurrences and the block mask of RainFusion2.0, section 3.1 "Blockwise
  * Sparse".
  *

@@ -23,8 +23,8 @@ What it computes, step by step, in the pages' order:
      P = exp(S - max S) lies in [0, 1], and a fixed scale 1/15 with zero-point
      -8 maps it onto the whole INT4 range [-8, 7]; then integer P.V against
      per-channel INT4 V with the zero-point correction 8 * column-sum.
-  5. Selective FP16 fallback for accuracy-sensitive blocks and heads
-     (RotateAttention abstract), using the block mask of RainFusion2.0
+  5. An FP16 path for the blocks and heads where INT4 would lose too much
+     accuracy (RotateAttention abstract), using the block mask of RainFusion2.0
      section 3.1 (a tile is skipped by one path and computed by the other),
      and a log-sum-exp merge of the two partial results.
   6. Block-sparse attention (RainFusion2.0 sections 3.1, 3.2, 3.4): block
